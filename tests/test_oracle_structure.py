@@ -1,0 +1,74 @@
+"""Pins of the oracle's model structure against numbers the pages print."""
+
+import numpy as np
+
+from oracle import ModelConfig, manifest, param_count
+from oracle import model as om
+from oracle.manifest import block_prefixes
+
+
+def _n(shape):
+    return int(np.prod(shape))
+
+
+def test_param_total_matches_page(golden):
+    pc = golden["page_constants"]
+    assert param_count(ModelConfig()) == pc["transformer_params"]["value"]
+
+
+def test_key_count_matches_page(golden):
+    keys = [k for k, _ in manifest(ModelConfig())]
+    assert len(keys) == golden["page_constants"]["checkpoint_keys"]["value"]
+    assert len(set(keys)) == len(keys)
+
+
+def test_final_layer_size(golden):
+    pc = golden["page_constants"]
+    m = dict(manifest(ModelConfig()))
+    fl = sum(_n(s) for k, s in m.items() if k.startswith("final_layer."))
+    assert abs(fl - pc["final_layer_params"]["value"]) <= pc["final_layer_params"]["rel_tol"] * 1.2e6
+    assert list(m["final_layer.linear.weight"]) == pc["final_layer_linear_shape"]["value"]
+
+
+def test_storage_sizes(golden):
+    pc = golden["page_constants"]
+    n = param_count(ModelConfig())
+    assert round(n * 2 / 1e9, 2) == pc["transformer_bf16_GB"]["value"]
+    assert round(n * 4 / 1e9, 1) == pc["transformer_fp32_GB"]["value"]
+
+
+def test_block_and_postnorm_counts(golden):
+    pc = golden["page_constants"]
+    cfg = ModelConfig()
+    keys = [k for k, _ in manifest(cfg)]
+    attn_blocks = [k for k in keys if k.endswith("attention.to_out.0.weight")]
+    post_normed = attn_blocks + [k for k in keys if k.endswith("feed_forward.w2.weight")]
+    assert len(attn_blocks) == pc["attention_blocks"]["value"]
+    assert len(post_normed) == pc["post_normed_projections"]["value"]
+    # every projection feeding an RMSNorm has its norm weight
+    for k in post_normed:
+        prefix = k.split(".attention.")[0].split(".feed_forward.")[0]
+        assert f"{prefix}.attention_norm2.weight" in keys
+        assert f"{prefix}.ffn_norm2.weight" in keys
+    # context refiner is unmodulated, the other 32 blocks are modulated
+    mods = [p for p, m in block_prefixes(cfg) if m]
+    assert len(mods) == 32
+    assert all(not p.startswith("context_refiner") for p in mods)
+
+
+def test_architecture_constants(golden):
+    pc = golden["page_constants"]
+    cfg = ModelConfig()
+    assert cfg.hidden == pc["hidden"]["value"]
+    assert cfg.n_heads == pc["heads"]["value"]
+    assert cfg.ffn == pc["ffn"]["value"]
+    assert list(cfg.rope_axes) == pc["rope_axes"]["value"]
+    assert sum(cfg.rope_axes) == cfg.head_dim == 128
+
+
+def test_image_token_counts(golden):
+    it = golden["page_constants"]["image_tokens"]
+    for res, n in it["value"].items():
+        C, Hl, Wl = it["latent"][res]
+        tok = om.patchify(np.zeros((C, Hl, Wl)), 2)
+        assert tok.shape == (n, 64)
