@@ -1,0 +1,12 @@
+"""Z-Image S3-DiT denoiser forward on AMD MI355X (gfx950).
+
+The engine is the C-ABI library ``libzimg_dit.so`` (include/zimg_dit.h,
+include/zimg_ops.h) with hand-written HIP kernels; this package is its thin
+ctypes binding plus the FlowMatch Euler driver.
+"""
+
+from . import binding
+from .binding import DiT, ZimgError, config, manifest
+from .sampler import euler_loop, schedule
+
+__all__ = ["binding", "DiT", "ZimgError", "config", "manifest", "euler_loop", "schedule"]

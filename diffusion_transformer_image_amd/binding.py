@@ -1,0 +1,284 @@
+"""ctypes binding of libzimg_dit.so (include/zimg_dit.h, include/zimg_ops.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels.  Device buffers are torch CUDA tensors (PyTorch provides device
+memory and streams); host arrays are numpy.  The library must have been
+built (``python -m diffusion_transformer_image_amd.build``); loading fails
+loudly otherwise -- there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzimg_dit.so")
+
+ZIMG_OK = 0
+ZIMG_EINVAL = -1
+ZIMG_EWEIGHT = -2
+ZIMG_EUNSUPPORTED = -3
+ZIMG_ENOMEM = -4
+ZIMG_EHIP = -5
+ZIMG_ESTATE = -6
+ZIMG_F32 = 0
+ZIMG_BF16 = 1
+EPI_BF16 = 0
+EPI_F32_BIAS = 1
+EPI_SWIGLU = 2
+
+_CODES = {ZIMG_EINVAL: "EINVAL", ZIMG_EWEIGHT: "EWEIGHT", ZIMG_EUNSUPPORTED: "EUNSUPPORTED",
+          ZIMG_ENOMEM: "ENOMEM", ZIMG_EHIP: "EHIP", ZIMG_ESTATE: "ESTATE"}
+
+
+class ZimgError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"zimg error {_CODES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("ffn", ctypes.c_int32),
+        ("n_layers", ctypes.c_int32), ("n_noise_refiner", ctypes.c_int32),
+        ("n_context_refiner", ctypes.c_int32), ("in_channels", ctypes.c_int32),
+        ("patch", ctypes.c_int32), ("cap_feat_dim", ctypes.c_int32), ("adaln_dim", ctypes.c_int32),
+        ("t_mid", ctypes.c_int32), ("rope_axes", ctypes.c_int32 * 3), ("rope_theta", ctypes.c_float),
+        ("t_scale", ctypes.c_float), ("max_period", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("final_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
+        ("max_image_tokens", ctypes.c_int32), ("max_caption_tokens", ctypes.c_int32),
+    ]
+
+    def as_dict(self):
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["rope_axes"] = tuple(self.rope_axes)
+        return d
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_F32P = ctypes.POINTER(ctypes.c_float)
+
+# name -> (restype, argtypes); the exported C ABI
+SIGNATURES = {
+    "zimg_last_error": (ctypes.c_char_p, []),
+    "zimg_dit_default_config": (None, [ctypes.POINTER(Config)]),
+    "zimg_dit_check_config": (_I32, [ctypes.POINTER(Config)]),
+    "zimg_dit_manifest_size": (_I32, [ctypes.POINTER(Config), _I32P]),
+    "zimg_dit_manifest_entry": (_I32, [ctypes.POINTER(Config), _I32, ctypes.POINTER(ctypes.c_char_p), _I32P,
+                                       ctypes.POINTER(ctypes.c_int64)]),
+    "zimg_dit_create": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(Tensor), _I32, ctypes.POINTER(_P)]),
+    "zimg_dit_alloc": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(_P)]),
+    "zimg_dit_set_weight": (_I32, [_P, ctypes.POINTER(Tensor)]),
+    "zimg_dit_finalize": (_I32, [_P]),
+    "zimg_dit_forward": (_I32, [_P, _P, _I32, _I32, _I32, _P, _I32, _I32P, _F32P, _P, _P]),
+    "zimg_dit_destroy": (None, [_P]),
+    "zimg_dit_last_error": (ctypes.c_char_p, [_P]),
+    "zimg_dit_set_capture": (_I32, [_P, _P, ctypes.c_size_t]),
+    "zimg_position_ids": (_I32, [_I32, _I32, _I32, _I32P, _I32P]),
+    "zimg_rope_tables": (_I32, [ctypes.POINTER(Config), _I32P, _I64, _F32P, _F32P]),
+    "zimg_row_layout": (_I32, [_I32, _I32, _I32P, _I32P, _I32P, _I32P]),
+    "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
+    "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
+    "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m diffusion_transformer_image_amd.build` (there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc, handle=None):
+    if rc != ZIMG_OK:
+        msg = lib().zimg_last_error().decode()
+        if not msg and handle:
+            msg = lib().zimg_dit_last_error(handle).decode()
+        raise ZimgError(rc, msg)
+
+
+def config(**overrides):
+    c = Config()
+    lib().zimg_dit_default_config(ctypes.byref(c))
+    for k, v in overrides.items():
+        if k == "rope_axes":
+            c.rope_axes = (ctypes.c_int32 * 3)(*v)
+        elif k in dict(Config._fields_):
+            setattr(c, k, v)
+        else:
+            raise KeyError(f"unknown config field {k}")
+    return c
+
+
+def check_config(cfg):
+    _check(lib().zimg_dit_check_config(ctypes.byref(cfg)))
+
+
+def manifest(cfg):
+    """[(name, shape)] the engine expects, in canonical order."""
+    n = ctypes.c_int32()
+    _check(lib().zimg_dit_manifest_size(ctypes.byref(cfg), ctypes.byref(n)))
+    out = []
+    for i in range(n.value):
+        name = ctypes.c_char_p()
+        nd = ctypes.c_int32()
+        shp = (ctypes.c_int64 * 4)()
+        _check(lib().zimg_dit_manifest_entry(ctypes.byref(cfg), i, ctypes.byref(name), ctypes.byref(nd), shp))
+        out.append((name.value.decode(), tuple(shp[:nd.value])))
+    return out
+
+
+def _tensor(name, arr):
+    """Tensor descriptor for a host numpy array (float32 or uint16 bf16 bits)."""
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.float32:
+        dt = ZIMG_F32
+    elif a.dtype == np.uint16:
+        dt = ZIMG_BF16
+    else:
+        raise TypeError(f"{name}: weights must be float32 or uint16 bf16 bits, got {a.dtype}")
+    t = Tensor()
+    t.name = name.encode()
+    t.data = a.ctypes.data
+    t.dtype = dt
+    t.ndim = a.ndim
+    for i, s in enumerate(a.shape):
+        t.shape[i] = s
+    return t, a
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class DiT:
+    """Handle of one engine instance (device weights + workspace)."""
+
+    def __init__(self, cfg, weights):
+        """``weights``: iterable of (name, numpy array) or a mapping."""
+        self.cfg = cfg
+        self._h = ctypes.c_void_p()
+        _check(lib().zimg_dit_alloc(ctypes.byref(cfg), ctypes.byref(self._h)))
+        try:
+            items = weights.items() if hasattr(weights, "items") else weights
+            for name, arr in items:
+                t, keep = _tensor(name, arr)
+                _check(lib().zimg_dit_set_weight(self._h, ctypes.byref(t)), self._h)
+                del keep
+            _check(lib().zimg_dit_finalize(self._h), self._h)
+        except Exception:
+            self.close()
+            raise
+        self._capture = None
+
+    def close(self):
+        if self._h:
+            lib().zimg_dit_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def n_blocks(self):
+        c = self.cfg
+        return c.n_layers + c.n_noise_refiner + c.n_context_refiner
+
+    def forward(self, latent, caption_feats, caption_lens, t, out, stream=None):
+        """latent, caption_feats, out: torch CUDA tensors (fp32 latent/out,
+        fp32 or bf16 packed captions); caption_lens, t: host sequences."""
+        B, C, Hl, Wl = latent.shape
+        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
+        tt = np.ascontiguousarray(t, dtype=np.float32)
+        import torch
+        cap_dt = ZIMG_BF16 if caption_feats.dtype == torch.bfloat16 else ZIMG_F32
+        _check(lib().zimg_dit_forward(self._h, _ptr(latent), B, Hl, Wl, _ptr(caption_feats), cap_dt,
+                                      lens.ctypes.data_as(_I32P), tt.ctypes.data_as(_F32P), _ptr(out),
+                                      _stream(stream)), self._h)
+        return out
+
+    def run_blocks(self, x, B, Hl, Wl, caption_lens, t, first, n, stream=None):
+        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
+        tt = np.ascontiguousarray(t, dtype=np.float32)
+        _check(lib().zimg_dit_run_blocks(self._h, _ptr(x), B, Hl, Wl, lens.ctypes.data_as(_I32P),
+                                         tt.ctypes.data_as(_F32P), first, n, _stream(stream)), self._h)
+        return x
+
+    def set_capture(self, buf):
+        """buf: torch CUDA fp32 tensor or None."""
+        self._capture = buf
+        if buf is None:
+            _check(lib().zimg_dit_set_capture(self._h, None, 0), self._h)
+        else:
+            _check(lib().zimg_dit_set_capture(self._h, _ptr(buf), buf.numel() * 4), self._h)
+
+
+def row_layout(B, n_image_tokens, caption_lens):
+    lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
+    img = np.zeros(B, np.int32)
+    cap = np.zeros(B, np.int32)
+    S = ctypes.c_int32()
+    _check(lib().zimg_row_layout(B, n_image_tokens, lens.ctypes.data_as(_I32P), img.ctypes.data_as(_I32P),
+                                 cap.ctypes.data_as(_I32P), ctypes.byref(S)))
+    return img, cap, S.value
+
+
+def position_ids(L, Hp, Wp):
+    cap = np.zeros((L, 3), np.int32)
+    img = np.zeros((Hp * Wp, 3), np.int32)
+    _check(lib().zimg_position_ids(L, Hp, Wp, cap.ctypes.data_as(_I32P), img.ctypes.data_as(_I32P)))
+    return cap, img
+
+
+def rope_tables(cfg, ids):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    S = ids.shape[0]
+    cs = np.zeros((S, 64), np.float32)
+    sn = np.zeros((S, 64), np.float32)
+    _check(lib().zimg_rope_tables(ctypes.byref(cfg), ids.ctypes.data_as(_I32P), S, cs.ctypes.data_as(_F32P),
+                                  sn.ctypes.data_as(_F32P)))
+    return cs, sn
+
+
+def gemm_bf16(A, W, C, epilogue=EPI_BF16, bias=None, stream=None):
+    """C = epilogue(A W^T) on torch CUDA tensors (A, W bf16; C bf16 or fp32)."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().zimg_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), _ptr(C), C.stride(0), M, N, K,
+                                epilogue, _ptr(bias) if bias is not None else None, _stream(stream)))
+    return C
+
+
+def euler_step(x, model_out, dt, stream=None):
+    _check(lib().zimg_euler_step(_ptr(x), _ptr(model_out), float(dt), x.numel(), _stream(stream)))
+    return x

@@ -1,0 +1,73 @@
+// Shared device-side definitions for the gfx950 kernels of the S3-DiT engine.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ZI_DEV __device__ __forceinline__
+
+// bf16 <-> fp32.  The float -> bf16 cast rounds to nearest even (one
+// v_cvt_pk_bf16_f32 per pair on gfx950).
+ZI_DEV float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+ZI_DEV bf16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(bf16_t, b);
+}
+ZI_DEV uint32_t pack2bf(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// v_mfma_f32_32x32x16_bf16.  Lane l supplies A row (l % 32), k = (l/32)*8 + [0,8);
+// B column (l % 32), same k; accumulator element i*4+j of lane l is
+// C[i*8 + (l/32)*4 + j][l % 32].  (Layout checked on gfx950.)
+ZI_DEV f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+ZI_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+ZI_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over a whole workgroup of NT threads (NT a multiple of 64); ``red`` is
+// LDS scratch of NT/64 floats.  Every thread gets the total.
+template <int NT>
+ZI_DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8).  Renumber so that each XCD receives a contiguous range of
+// logical ids, keeping tiles that share operands in one L2.
+ZI_DEV int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid & 7;
+  const int idx = bid >> 3;
+  const int per = nblocks >> 3;
+  const int rem = nblocks & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}

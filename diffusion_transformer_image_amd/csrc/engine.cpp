@@ -1,0 +1,1062 @@
+// Host engine of the S3-DiT forward behind the C ABI of include/zimg_dit.h.
+//
+// What it owns: the model's weights on the device in the layout the kernels
+// want (bf16 matrices, fp32 vectors, q|k|v fused, w1/w3 interleaved in
+// groups of 32 rows, every block's adaLN projection concatenated into one
+// matrix), the whole forward workspace (sized at create, never allocated
+// inside a forward), the host-built RoPE tables and attention work lists
+// (cached per input geometry), and the block schedule.
+//
+// Row layout of the sequence buffer: all image rows of the batch (sample b
+// at b*Npad, Npad = image tokens rounded up to 16), then all caption rows
+// (sample b at its own offset, lengths rounded up to 16).  Padding rows
+// belong to no attention segment, so they never influence real rows.  The
+// noise refiner works on the image rows, the context refiner on the
+// caption rows, the joint blocks on all rows ("Z-Image" (AI Toolkit docs),
+// Architecture: text and image tokens share one sequence; 2 noise-refiner
+// blocks on image tokens, 2 context-refiner blocks on text tokens).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "../../include/zimg_dit.h"
+#include "../../include/zimg_ops.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_err(int code, const char* fmt, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return set_err(ZIMG_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
+  } while (0)
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+uint16_t f32_to_bf16(float f) {
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_to_f32(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+// ------------------------------------------------------------------ manifest
+
+struct ManifestEntry {
+  std::string name;
+  int ndim;
+  int64_t shape[4];
+};
+
+struct BlockSpec {
+  std::string prefix;
+  int stage;      // 0 noise refiner, 1 context refiner, 2 joint
+  bool modulated;
+};
+
+std::vector<BlockSpec> block_specs(const zimg_dit_config& c) {
+  std::vector<BlockSpec> v;
+  for (int i = 0; i < c.n_noise_refiner; ++i) v.push_back({"noise_refiner." + std::to_string(i), 0, true});
+  for (int i = 0; i < c.n_context_refiner; ++i) v.push_back({"context_refiner." + std::to_string(i), 1, false});
+  for (int i = 0; i < c.n_layers; ++i) v.push_back({"layers." + std::to_string(i), 2, true});
+  return v;
+}
+
+std::vector<ManifestEntry> build_manifest(const zimg_dit_config& c) {
+  const int64_t D = c.hidden, F = c.ffn, P = (int64_t)c.patch * c.patch * c.in_channels;
+  std::vector<ManifestEntry> m;
+  auto add = [&](const std::string& n, std::initializer_list<int64_t> s) {
+    ManifestEntry e;
+    e.name = n;
+    e.ndim = (int)s.size();
+    int i = 0;
+    for (int64_t v : s) e.shape[i++] = v;
+    for (; i < 4; ++i) e.shape[i] = 0;
+    m.push_back(e);
+  };
+  add("t_embedder.mlp.0.weight", {c.t_mid, c.adaln_dim});
+  add("t_embedder.mlp.0.bias", {c.t_mid});
+  add("t_embedder.mlp.2.weight", {c.adaln_dim, c.t_mid});
+  add("t_embedder.mlp.2.bias", {c.adaln_dim});
+  add("cap_embedder.0.weight", {c.cap_feat_dim});
+  add("cap_embedder.1.weight", {D, c.cap_feat_dim});
+  add("cap_embedder.1.bias", {D});
+  add("x_embedder.weight", {D, P});
+  add("x_embedder.bias", {D});
+  add("final_layer.adaLN_modulation.1.weight", {D, c.adaln_dim});
+  add("final_layer.adaLN_modulation.1.bias", {D});
+  add("final_layer.linear.weight", {P, D});
+  add("final_layer.linear.bias", {P});
+  add("x_pad_token", {1, D});
+  add("cap_pad_token", {1, D});
+  for (const auto& b : block_specs(c)) {
+    const std::string& p = b.prefix;
+    add(p + ".attention.to_q.weight", {D, D});
+    add(p + ".attention.to_k.weight", {D, D});
+    add(p + ".attention.to_v.weight", {D, D});
+    add(p + ".attention.to_out.0.weight", {D, D});
+    add(p + ".attention.norm_q.weight", {128});
+    add(p + ".attention.norm_k.weight", {128});
+    add(p + ".feed_forward.w1.weight", {F, D});
+    add(p + ".feed_forward.w2.weight", {D, F});
+    add(p + ".feed_forward.w3.weight", {F, D});
+    add(p + ".attention_norm1.weight", {D});
+    add(p + ".attention_norm2.weight", {D});
+    add(p + ".ffn_norm1.weight", {D});
+    add(p + ".ffn_norm2.weight", {D});
+    if (b.modulated) {
+      add(p + ".adaLN_modulation.0.weight", {4 * D, c.adaln_dim});
+      add(p + ".adaLN_modulation.0.bias", {4 * D});
+    }
+  }
+  return m;
+}
+
+// manifests are cached per config so that entry names stay valid
+std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>>& manifest_cache() {
+  static std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>> m;
+  return m;
+}
+const std::vector<ManifestEntry>& cached_manifest(const zimg_dit_config& c) {
+  std::string key((const char*)&c, sizeof c);
+  auto& mc = manifest_cache();
+  auto it = mc.find(key);
+  if (it == mc.end()) it = mc.emplace(key, std::make_unique<std::vector<ManifestEntry>>(build_manifest(c))).first;
+  return *it->second;
+}
+
+int check_config(const zimg_dit_config* c) {
+  if (!c) return set_err(ZIMG_EINVAL, "config is NULL");
+  if (c->n_heads <= 0 || c->hidden != c->n_heads * 128)
+    return set_err(ZIMG_EUNSUPPORTED, "hidden (%d) must equal n_heads (%d) * 128", c->hidden, c->n_heads);
+  if (c->hidden % 256 || c->hidden > 4096)
+    return set_err(ZIMG_EUNSUPPORTED, "hidden must be a multiple of 256 and at most 4096 (got %d)", c->hidden);
+  if (c->ffn <= 0 || c->ffn % 128)
+    return set_err(ZIMG_EUNSUPPORTED, "ffn must be a positive multiple of 128 (got %d)", c->ffn);
+  if (c->n_layers < 0 || c->n_noise_refiner < 0 || c->n_context_refiner < 0 ||
+      c->n_layers + c->n_noise_refiner + c->n_context_refiner == 0)
+    return set_err(ZIMG_EINVAL, "block counts must be >= 0 with at least one block");
+  if (c->in_channels <= 0 || c->patch <= 0 || (c->patch * c->patch * c->in_channels) % 64)
+    return set_err(ZIMG_EUNSUPPORTED, "patch*patch*in_channels must be a positive multiple of 64");
+  if (c->cap_feat_dim <= 0 || c->cap_feat_dim % 256 || c->cap_feat_dim > 4096)
+    return set_err(ZIMG_EUNSUPPORTED, "cap_feat_dim must be a multiple of 256 up to 4096 (got %d)", c->cap_feat_dim);
+  if (c->adaln_dim <= 0 || c->adaln_dim % 256)
+    return set_err(ZIMG_EUNSUPPORTED, "adaln_dim must be a positive multiple of 256 (got %d)", c->adaln_dim);
+  if (c->t_mid <= 0 || c->t_mid % 256)
+    return set_err(ZIMG_EUNSUPPORTED, "t_mid must be a positive multiple of 256 (got %d)", c->t_mid);
+  if (c->rope_axes[0] + c->rope_axes[1] + c->rope_axes[2] != 128 || (c->rope_axes[0] | c->rope_axes[1] | c->rope_axes[2]) & 1 ||
+      c->rope_axes[0] <= 0 || c->rope_axes[1] <= 0 || c->rope_axes[2] <= 0)
+    return set_err(ZIMG_EUNSUPPORTED, "rope_axes must be positive, even and sum to 128");
+  if (!(c->rope_theta > 0) || !std::isfinite(c->rope_theta) || !(c->t_scale > 0) || !std::isfinite(c->t_scale) ||
+      !(c->max_period > 1) || !std::isfinite(c->max_period))
+    return set_err(ZIMG_EINVAL, "rope_theta, t_scale must be positive and max_period > 1");
+  if (!(c->norm_eps > 0) || !(c->final_eps > 0) || !std::isfinite(c->norm_eps) || !std::isfinite(c->final_eps))
+    return set_err(ZIMG_EINVAL, "norm_eps and final_eps must be positive");
+  if (c->max_batch < 1 || c->max_batch > 64) return set_err(ZIMG_EINVAL, "max_batch must be 1..64");
+  if (c->max_image_tokens < 1 || c->max_image_tokens > (1 << 20))
+    return set_err(ZIMG_EINVAL, "max_image_tokens must be 1..1048576");
+  if (c->max_caption_tokens < 1 || c->max_caption_tokens > 512)
+    return set_err(ZIMG_EUNSUPPORTED, "max_caption_tokens must be 1..512 (the caption limit of the model)");
+  return ZIMG_OK;
+}
+
+// ------------------------------------------------------------------ host tables
+
+void position_ids(int L, int Hp, int Wp, int32_t* cap, int32_t* img) {
+  for (int k = 0; k < L; ++k) {
+    cap[3 * k] = k + 1;
+    cap[3 * k + 1] = 0;
+    cap[3 * k + 2] = 0;
+  }
+  for (int i = 0; i < Hp; ++i)
+    for (int j = 0; j < Wp; ++j) {
+      int32_t* r = img + 3 * (i * Wp + j);
+      r[0] = L + 1;
+      r[1] = i;
+      r[2] = j;
+    }
+}
+
+// omega per pair and the axis it belongs to
+void rope_freqs(const zimg_dit_config& c, double* omega, int* axis) {
+  int p = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int d = c.rope_axes[a];
+    for (int r = 0; r < d / 2; ++r, ++p) {
+      omega[p] = std::pow((double)c.rope_theta, -(2.0 * r) / (double)d);
+      axis[p] = a;
+    }
+  }
+}
+
+void rope_rows(const double* omega, const int* axis, const int32_t* ids, int64_t n, float* cs, float* sn) {
+  for (int64_t s = 0; s < n; ++s)
+    for (int p = 0; p < 64; ++p) {
+      const double phi = (double)ids[3 * s + axis[p]] * omega[p];
+      cs[s * 64 + p] = (float)std::cos(phi);
+      sn[s * 64 + p] = (float)std::sin(phi);
+    }
+}
+
+// ------------------------------------------------------------------ layout
+
+struct Layout {
+  int B = 0, Hl = 0, Wl = 0, Hp = 0, Wp = 0, N = 0, Npad = 0;
+  std::vector<int> lens, img_off, cap_off;
+  int cap_base = 0, S = 0, Lsum = 0;
+};
+
+Layout make_layout(int B, int Hl, int Wl, int patch, const int32_t* lens) {
+  Layout L;
+  L.B = B;
+  L.Hl = Hl;
+  L.Wl = Wl;
+  L.Hp = Hl / patch;
+  L.Wp = Wl / patch;
+  L.N = L.Hp * L.Wp;
+  L.Npad = (int)round_up(L.N, 16);
+  L.cap_base = B * L.Npad;
+  int off = L.cap_base;
+  for (int b = 0; b < B; ++b) {
+    L.lens.push_back(lens[b]);
+    L.img_off.push_back(b * L.Npad);
+    L.cap_off.push_back(off);
+    off += (int)round_up(lens[b], 16);
+    L.Lsum += lens[b];
+  }
+  L.S = off;
+  return L;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ engine
+
+struct zimg_dit {
+  zimg_dit_config cfg{};
+  std::string err;
+  int device = 0;
+  std::vector<ManifestEntry> manifest;
+  std::vector<BlockSpec> blocks;
+  std::vector<int> mod_index;  // per block, -1 if unmodulated
+  int n_mod = 0;
+  int64_t mod_stride = 0;
+  bool finalized = false;
+
+  struct BlockW {
+    bf16_t *wqkv = nullptr, *wo = nullptr, *w13 = nullptr, *w2 = nullptr;
+    float *an1 = nullptr, *an2 = nullptr, *fn1 = nullptr, *fn2 = nullptr, *nq = nullptr, *nk = nullptr;
+  };
+  std::vector<BlockW> bw;
+  bf16_t *t1w = nullptr, *t2w = nullptr, *cap_w = nullptr, *x_w = nullptr, *fin_w = nullptr, *ada_w = nullptr;
+  float *t1b = nullptr, *t2b = nullptr, *capn_w = nullptr, *cap_b = nullptr, *x_b = nullptr, *fin_b = nullptr,
+        *ada_b = nullptr, *pad_x = nullptr, *pad_cap = nullptr;
+
+  // weight slots
+  struct Slot {
+    int kind;  // 0 bf16 matrix, 1 f32 vector, 2 w1 (interleave first), 3 w3 (interleave second)
+    void* dst;
+    int64_t rows, cols;
+    bool set = false;
+  };
+  std::map<std::string, Slot> slots;
+
+  // workspace
+  int64_t S_max = 0, S_pad = 0, img_rows_max = 0, cap_rows_max = 0;
+  float* x = nullptr;
+  bf16_t *h = nullptr, *qkv = nullptr, *vT = nullptr, *o = nullptr, *y = nullptr, *g = nullptr, *xin = nullptr,
+         *capn = nullptr;
+  float *temb = nullptr, *hmid = nullptr, *cvec = nullptr, *mod = nullptr;
+  float *cos_t = nullptr, *sin_t = nullptr;
+  int32_t* row_sample = nullptr;
+  zimg::AttnSeg* segs = nullptr;    // [3][max_batch]
+  zimg::AttnItem* items = nullptr;  // [3][max_items]
+  int64_t max_items = 0;
+
+  // host staging for tables (pinned) and the cached geometry key
+  void* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t staging_done = nullptr;
+  std::vector<int32_t> table_key;
+  int n_items_stage[3] = {0, 0, 0};
+
+  // capture
+  float* cap_buf = nullptr;
+  size_t cap_bytes = 0;
+
+  std::vector<void*> allocations;
+
+  int fail(int code) {
+    err = g_last_error;
+    return code;
+  }
+  template <class T>
+  int dalloc(T** p, size_t count) {
+    void* q = nullptr;
+    const size_t bytes = count * sizeof(T);
+    hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+    if (e != hipSuccess)
+      return set_err(e == hipErrorOutOfMemory ? ZIMG_ENOMEM : ZIMG_EHIP, "hipMalloc(%zu) failed: %s", bytes,
+                     hipGetErrorString(e));
+    allocations.push_back(q);
+    e = hipMemset(q, 0, bytes ? bytes : 16);
+    if (e != hipSuccess) return set_err(ZIMG_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
+    *p = (T*)q;
+    return ZIMG_OK;
+  }
+
+  ~zimg_dit() {
+    for (void* p : allocations) (void)hipFree(p);
+    if (staging) (void)hipHostFree(staging);
+    if (staging_done) (void)hipEventDestroy(staging_done);
+  }
+
+  int allocate();
+  int set_weight(const zimg_tensor* w);
+  int finalize();
+  int prepare(const Layout& L, const float* t, hipStream_t s);
+  int run_block(int bi, const Layout& L, bool h_ready, int next, hipStream_t s);
+  int forward(const float* latent, const Layout& L, const void* caps, int cap_dtype, const float* t, float* out,
+              hipStream_t s);
+  int run_blocks(float* x_io, const Layout& L, const float* t, int first, int n, hipStream_t s);
+};
+
+int zimg_dit::allocate() {
+  const zimg_dit_config& c = cfg;
+  const int64_t D = c.hidden, F = c.ffn, P = (int64_t)c.patch * c.patch * c.in_channels;
+  manifest = cached_manifest(c);
+  blocks = block_specs(c);
+  for (auto& b : blocks) mod_index.push_back(b.modulated ? n_mod++ : -1);
+  mod_stride = (int64_t)n_mod * 4 * D + D;
+  bw.resize(blocks.size());
+  int rc;
+#define ALLOC(p, n) \
+  if ((rc = dalloc(&(p), (size_t)(n))) != ZIMG_OK) return rc
+  ALLOC(t1w, (int64_t)c.t_mid * c.adaln_dim);
+  ALLOC(t1b, c.t_mid);
+  ALLOC(t2w, (int64_t)c.adaln_dim * c.t_mid);
+  ALLOC(t2b, c.adaln_dim);
+  ALLOC(capn_w, c.cap_feat_dim);
+  ALLOC(cap_w, D * c.cap_feat_dim);
+  ALLOC(cap_b, D);
+  ALLOC(x_w, D * P);
+  ALLOC(x_b, D);
+  ALLOC(fin_w, P * D);
+  ALLOC(fin_b, P);
+  ALLOC(pad_x, D);
+  ALLOC(pad_cap, D);
+  ALLOC(ada_w, mod_stride * c.adaln_dim);
+  ALLOC(ada_b, mod_stride);
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    BlockW& w = bw[i];
+    ALLOC(w.wqkv, 3 * D * D);
+    ALLOC(w.wo, D * D);
+    ALLOC(w.w13, 2 * F * D);
+    ALLOC(w.w2, D * F);
+    ALLOC(w.an1, D);
+    ALLOC(w.an2, D);
+    ALLOC(w.fn1, D);
+    ALLOC(w.fn2, D);
+    ALLOC(w.nq, 128);
+    ALLOC(w.nk, 128);
+  }
+
+  // slots, named as in the manifest
+  auto mat = [&](const std::string& n, void* d, int64_t r, int64_t cc, int kind = 0) {
+    slots[n] = Slot{kind, d, r, cc, false};
+  };
+  auto vec = [&](const std::string& n, float* d, int64_t len) { slots[n] = Slot{1, d, 1, len, false}; };
+  mat("t_embedder.mlp.0.weight", t1w, c.t_mid, c.adaln_dim);
+  vec("t_embedder.mlp.0.bias", t1b, c.t_mid);
+  mat("t_embedder.mlp.2.weight", t2w, c.adaln_dim, c.t_mid);
+  vec("t_embedder.mlp.2.bias", t2b, c.adaln_dim);
+  vec("cap_embedder.0.weight", capn_w, c.cap_feat_dim);
+  mat("cap_embedder.1.weight", cap_w, D, c.cap_feat_dim);
+  vec("cap_embedder.1.bias", cap_b, D);
+  mat("x_embedder.weight", x_w, D, P);
+  vec("x_embedder.bias", x_b, D);
+  mat("final_layer.adaLN_modulation.1.weight", ada_w + (int64_t)n_mod * 4 * D * c.adaln_dim, D, c.adaln_dim);
+  vec("final_layer.adaLN_modulation.1.bias", ada_b + (int64_t)n_mod * 4 * D, D);
+  mat("final_layer.linear.weight", fin_w, P, D);
+  vec("final_layer.linear.bias", fin_b, P);
+  vec("x_pad_token", pad_x, D);
+  vec("cap_pad_token", pad_cap, D);
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    const std::string& p = blocks[i].prefix;
+    BlockW& w = bw[i];
+    mat(p + ".attention.to_q.weight", w.wqkv, D, D);
+    mat(p + ".attention.to_k.weight", w.wqkv + D * D, D, D);
+    mat(p + ".attention.to_v.weight", w.wqkv + 2 * D * D, D, D);
+    mat(p + ".attention.to_out.0.weight", w.wo, D, D);
+    vec(p + ".attention.norm_q.weight", w.nq, 128);
+    vec(p + ".attention.norm_k.weight", w.nk, 128);
+    mat(p + ".feed_forward.w1.weight", w.w13, F, D, 2);
+    mat(p + ".feed_forward.w3.weight", w.w13, F, D, 3);
+    mat(p + ".feed_forward.w2.weight", w.w2, D, F);
+    vec(p + ".attention_norm1.weight", w.an1, D);
+    vec(p + ".attention_norm2.weight", w.an2, D);
+    vec(p + ".ffn_norm1.weight", w.fn1, D);
+    vec(p + ".ffn_norm2.weight", w.fn2, D);
+    if (blocks[i].modulated) {
+      const int64_t k = mod_index[i];
+      mat(p + ".adaLN_modulation.0.weight", ada_w + k * 4 * D * c.adaln_dim, 4 * D, c.adaln_dim);
+      vec(p + ".adaLN_modulation.0.bias", ada_b + k * 4 * D, 4 * D);
+    }
+  }
+
+  // workspace
+  img_rows_max = (int64_t)c.max_batch * round_up(c.max_image_tokens, 16);
+  cap_rows_max = (int64_t)c.max_batch * round_up(c.max_caption_tokens, 16);
+  S_max = img_rows_max + cap_rows_max;
+  S_pad = round_up(S_max, 64) + 64;
+  ALLOC(x, S_max * D);
+  ALLOC(h, S_max * D);
+  ALLOC(qkv, S_max * 3 * D);
+  ALLOC(vT, (int64_t)c.n_heads * 128 * S_pad);
+  ALLOC(o, S_max * D);
+  ALLOC(y, S_max * D);
+  ALLOC(g, S_max * F);
+  ALLOC(xin, img_rows_max * P);
+  ALLOC(capn, cap_rows_max * c.cap_feat_dim);
+  ALLOC(temb, (int64_t)c.max_batch * c.adaln_dim);
+  ALLOC(hmid, (int64_t)c.max_batch * c.t_mid);
+  ALLOC(cvec, (int64_t)c.max_batch * c.adaln_dim);
+  ALLOC(mod, (int64_t)c.max_batch * mod_stride);
+  ALLOC(cos_t, S_max * 64);
+  ALLOC(sin_t, S_max * 64);
+  ALLOC(row_sample, S_max);
+  max_items = S_max / 16 + 2 * (int64_t)c.max_batch + 8;  // q-tiles of 128 over ranges of >= 16 rows
+  ALLOC(segs, 3 * (int64_t)c.max_batch);
+  ALLOC(items, 3 * max_items);
+#undef ALLOC
+  staging_bytes = (size_t)S_max * 64 * 4 * 2 + (size_t)S_max * 4 + 3 * c.max_batch * sizeof(zimg::AttnSeg) +
+                  3 * max_items * sizeof(zimg::AttnItem);
+  hipError_t e = hipHostMalloc(&staging, staging_bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return set_err(ZIMG_ENOMEM, "hipHostMalloc(%zu) failed: %s", staging_bytes, hipGetErrorString(e));
+  HIP_TRY(hipEventCreateWithFlags(&staging_done, hipEventDisableTiming));
+  HIP_TRY(hipEventRecord(staging_done, nullptr));
+  return ZIMG_OK;
+}
+
+int zimg_dit::set_weight(const zimg_tensor* w) {
+  if (!w || !w->name) return set_err(ZIMG_EINVAL, "weight tensor or its name is NULL");
+  auto it = slots.find(w->name);
+  if (it == slots.end()) return set_err(ZIMG_EWEIGHT, "unknown weight '%s'", w->name);
+  Slot& sl = it->second;
+  if (sl.set) return set_err(ZIMG_EWEIGHT, "duplicate weight '%s'", w->name);
+  const ManifestEntry* me = nullptr;
+  for (const auto& e : manifest)
+    if (e.name == w->name) me = &e;
+  if (!me || w->ndim != me->ndim) return set_err(ZIMG_EWEIGHT, "weight '%s' has rank %d, expected %d", w->name, w->ndim, me ? me->ndim : -1);
+  for (int i = 0; i < me->ndim; ++i)
+    if (w->shape[i] != me->shape[i])
+      return set_err(ZIMG_EWEIGHT, "weight '%s' dim %d is %lld, expected %lld", w->name, i, (long long)w->shape[i],
+                     (long long)me->shape[i]);
+  if (!w->data) return set_err(ZIMG_EINVAL, "weight '%s' has NULL data", w->name);
+  if (w->dtype != ZIMG_F32 && w->dtype != ZIMG_BF16) return set_err(ZIMG_EINVAL, "weight '%s' has unknown dtype %d", w->name, w->dtype);
+  const int64_t n = sl.rows * sl.cols;
+  if (sl.kind == 1) {
+    std::vector<float> v(n);
+    if (w->dtype == ZIMG_F32) std::memcpy(v.data(), w->data, n * 4);
+    else
+      for (int64_t i = 0; i < n; ++i) v[i] = bf16_to_f32(((const uint16_t*)w->data)[i]);
+    HIP_TRY(hipMemcpy(sl.dst, v.data(), n * 4, hipMemcpyHostToDevice));
+  } else {
+    std::vector<uint16_t> tmp;
+    const uint16_t* src = (const uint16_t*)w->data;
+    if (w->dtype == ZIMG_F32) {
+      tmp.resize(n);
+      const float* f = (const float*)w->data;
+      for (int64_t i = 0; i < n; ++i) tmp[i] = f32_to_bf16(f[i]);
+      src = tmp.data();
+    }
+    if (sl.kind == 0) {
+      HIP_TRY(hipMemcpy(sl.dst, src, n * 2, hipMemcpyHostToDevice));
+    } else {
+      // interleave 32-row groups: w1 rows go to 64g + r, w3 rows to 64g + 32 + r
+      const int64_t cols = sl.cols;
+      const int64_t half = sl.kind == 3 ? 32 : 0;
+      HIP_TRY(hipMemcpy2D((bf16_t*)sl.dst + half * cols, 64 * cols * 2, src, 32 * cols * 2, 32 * cols * 2,
+                          sl.rows / 32, hipMemcpyHostToDevice));
+    }
+  }
+  sl.set = true;
+  return ZIMG_OK;
+}
+
+int zimg_dit::finalize() {
+  std::string missing;
+  int nmiss = 0;
+  for (const auto& e : manifest)
+    if (!slots[e.name].set) {
+      if (nmiss < 5) missing += (missing.empty() ? "" : ", ") + e.name;
+      ++nmiss;
+    }
+  if (nmiss) return set_err(ZIMG_EWEIGHT, "%d weight(s) missing: %s%s", nmiss, missing.c_str(), nmiss > 5 ? ", ..." : "");
+  finalized = true;
+  return ZIMG_OK;
+}
+
+// Build (or reuse) the RoPE tables, row->sample map and attention work lists
+// for this geometry, then compute the timestep conditioning and every
+// block's modulation.
+int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
+  const zimg_dit_config& c = cfg;
+  std::vector<int32_t> key = {L.B, L.Hl, L.Wl};
+  for (int v : L.lens) key.push_back(v);
+  if (key != table_key) {
+    HIP_TRY(hipEventSynchronize(staging_done));  // previous upload has left the staging buffer
+    char* st = (char*)staging;
+    float* cs = (float*)st;
+    float* sn = cs + L.S * 64;
+    int32_t* rs = (int32_t*)(sn + L.S * 64);
+    zimg::AttnSeg* sg = (zimg::AttnSeg*)(rs + L.S);
+    zimg::AttnItem* itm = (zimg::AttnItem*)(sg + 3 * c.max_batch);
+    for (int64_t i = 0; i < (int64_t)L.S * 64; ++i) {
+      cs[i] = 1.0f;
+      sn[i] = 0.0f;
+    }
+    for (int i = 0; i < L.S; ++i) rs[i] = 0;
+    double omega[64];
+    int axis[64];
+    rope_freqs(c, omega, axis);
+    std::vector<int32_t> cap_ids, img_ids((size_t)L.N * 3);
+    for (int b = 0; b < L.B; ++b) {
+      cap_ids.assign((size_t)L.lens[b] * 3, 0);
+      position_ids(L.lens[b], L.Hp, L.Wp, cap_ids.data(), img_ids.data());
+      rope_rows(omega, axis, img_ids.data(), L.N, cs + (int64_t)L.img_off[b] * 64, sn + (int64_t)L.img_off[b] * 64);
+      rope_rows(omega, axis, cap_ids.data(), L.lens[b], cs + (int64_t)L.cap_off[b] * 64, sn + (int64_t)L.cap_off[b] * 64);
+      for (int i = 0; i < L.Npad; ++i) rs[L.img_off[b] + i] = b;
+      for (int i = 0; i < (int)round_up(L.lens[b], 16); ++i) rs[L.cap_off[b] + i] = b;
+    }
+    // segments and q-tiles of 128 rows per stage
+    for (int stg = 0; stg < 3; ++stg) {
+      int ni = 0;
+      for (int b = 0; b < L.B; ++b) {
+        zimg::AttnSeg& q = sg[stg * c.max_batch + b];
+        q = zimg::AttnSeg{{0, 0}, {0, 0}};
+        int k = 0;
+        if (stg != 1) {
+          q.r0[k] = L.img_off[b];
+          q.n[k++] = L.N;
+        }
+        if (stg != 0) {
+          q.r0[k] = L.cap_off[b];
+          q.n[k++] = L.lens[b];
+        }
+        for (int r = 0; r < k; ++r)
+          for (int q0 = 0; q0 < q.n[r]; q0 += 128) {
+            if (ni >= max_items) return set_err(ZIMG_EINVAL, "internal: attention work list overflow");
+            itm[stg * max_items + ni++] = zimg::AttnItem{q.r0[r] + q0, std::min(128, q.n[r] - q0), b, 0};
+          }
+      }
+      n_items_stage[stg] = ni;
+    }
+    HIP_TRY(hipMemcpyAsync(cos_t, cs, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(sin_t, sn, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(row_sample, rs, (size_t)L.S * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(segs, sg, 3 * c.max_batch * sizeof(zimg::AttnSeg), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(items, itm, 3 * max_items * sizeof(zimg::AttnItem), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(staging_done, s));
+    table_key = key;
+  }
+
+  // timestep embedding -> MLP -> every modulation vector
+  zimg::TimeArgs ta{};
+  for (int b = 0; b < L.B; ++b) ta.t[b] = t[b];
+  HIP_TRY(zimg::launch_timestep_embed(ta, L.B, c.adaln_dim, c.t_scale, c.max_period, temb, s));
+  HIP_TRY(zimg::launch_gemv(t1w, t1b, temb, c.adaln_dim, hmid, c.t_mid, c.t_mid, c.adaln_dim, L.B, 0, s));
+  HIP_TRY(zimg::launch_gemv(t2w, t2b, hmid, c.t_mid, cvec, c.adaln_dim, c.adaln_dim, c.t_mid, L.B, 1, s));
+  const int64_t D = c.hidden;
+  if (n_mod)
+    HIP_TRY(zimg::launch_gemv(ada_w, ada_b, cvec, c.adaln_dim, mod, mod_stride, (int)(n_mod * 4 * D), c.adaln_dim,
+                              L.B, 0, s));
+  HIP_TRY(zimg::launch_gemv(ada_w + n_mod * 4 * D * c.adaln_dim, ada_b + n_mod * 4 * D, cvec, c.adaln_dim,
+                            mod + n_mod * 4 * D, mod_stride, (int)D, c.adaln_dim, L.B, 1, s));
+  return ZIMG_OK;
+}
+
+static void stage_rows(const Layout& L, int stage, int& r0, int& r1) {
+  r0 = stage == 1 ? L.cap_base : 0;
+  r1 = stage == 0 ? L.cap_base : L.S;
+}
+
+// One block on rows of its stage.  ``h_ready``: h already holds this block's
+// modulated pre-norm (fused into the previous block's last kernel).
+// ``next``: 0 no fused follow-up, 1 the next block's pre-norm (same rows),
+// 2 the final layer's LayerNorm on the image rows.
+int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStream_t s) {
+  const zimg_dit_config& c = cfg;
+  const int D = c.hidden, F = c.ffn, H = c.n_heads;
+  const BlockW& w = bw[bi];
+  const int stage = blocks[bi].stage;
+  int r0, r1;
+  stage_rows(L, stage, r0, r1);
+  const int M = r1 - r0;
+  const int mi = mod_index[bi];
+  auto mref = [&](int chunk) {
+    return mi < 0 ? zimg::ModRef{nullptr, 0, 0} : zimg::ModRef{mod, mod_stride, (int)(mi * 4 * D + chunk * D)};
+  };
+  if (!h_ready) {
+    zimg::PreNormArgs pa{x, w.an1, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0};
+    HIP_TRY(zimg::launch_pre_norm(pa, s));
+  }
+  zimg::GemmArgs ga{};
+  ga.A = h + (int64_t)r0 * D;
+  ga.lda = D;
+  ga.W = w.wqkv;
+  ga.ldw = D;
+  ga.M = M;
+  ga.N = 3 * D;
+  ga.K = D;
+  ga.epi = zimg::EPI_BF16;
+  ga.ep.C = qkv + (int64_t)r0 * 3 * D;
+  ga.ep.ldc = 3 * D;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+
+  zimg::QKRopeArgs qa{qkv, vT, w.nq, w.nk, cos_t, sin_t, r0, r1, H, (int)S_pad, c.norm_eps};
+  HIP_TRY(zimg::launch_qknorm_rope(qa, s));
+
+  zimg::AttnArgs aa{qkv, vT, o, items + stage * max_items, segs + stage * c.max_batch, n_items_stage[stage], H,
+                    (int)S_pad, (float)(1.4426950408889634 / std::sqrt(128.0))};
+  HIP_TRY(zimg::launch_attention(aa, s));
+
+  ga.A = o + (int64_t)r0 * D;
+  ga.W = w.wo;
+  ga.N = D;
+  ga.ep.C = y + (int64_t)r0 * D;
+  ga.ep.ldc = D;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+
+  zimg::PostNormArgs pn{};
+  pn.x = x;
+  pn.y = y;
+  pn.w_post = w.an2;
+  pn.gate = mref(1);
+  pn.r0 = r0;
+  pn.r1 = r1;
+  pn.n0 = r0;
+  pn.n1 = r1;
+  pn.w_next = w.fn1;
+  pn.scale_next = mref(2);
+  pn.next_kind = 0;
+  pn.next_eps = c.norm_eps;
+  pn.row_sample = row_sample;
+  pn.h = h;
+  pn.D = D;
+  pn.eps = c.norm_eps;
+  HIP_TRY(zimg::launch_post_norm(pn, s));
+
+  ga.A = h + (int64_t)r0 * D;
+  ga.W = w.w13;
+  ga.N = 2 * F;
+  ga.epi = zimg::EPI_SWIGLU;
+  ga.ep.C = g + (int64_t)r0 * F;
+  ga.ep.ldc = F;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+
+  ga.A = g + (int64_t)r0 * F;
+  ga.lda = F;
+  ga.W = w.w2;
+  ga.ldw = F;
+  ga.N = D;
+  ga.K = F;
+  ga.epi = zimg::EPI_BF16;
+  ga.ep.C = y + (int64_t)r0 * D;
+  ga.ep.ldc = D;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+
+  pn.w_post = w.fn2;
+  pn.gate = mref(3);
+  if (next == 1) {
+    const int ni = bi + 1;
+    const int nmi = mod_index[ni];
+    pn.w_next = bw[ni].an1;
+    pn.scale_next = nmi < 0 ? zimg::ModRef{nullptr, 0, 0} : zimg::ModRef{mod, mod_stride, (int)(nmi * 4 * D)};
+    pn.next_kind = 0;
+    pn.next_eps = c.norm_eps;
+  } else if (next == 2) {
+    pn.n0 = 0;
+    pn.n1 = L.cap_base;
+    pn.w_next = nullptr;
+    pn.scale_next = zimg::ModRef{mod, mod_stride, (int)(n_mod * 4 * D)};
+    pn.next_kind = 1;
+    pn.next_eps = c.final_eps;
+  } else {
+    pn.n0 = pn.n1 = 0;
+  }
+  HIP_TRY(zimg::launch_post_norm(pn, s));
+  return ZIMG_OK;
+}
+
+int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, int cap_dtype, const float* t,
+                      float* out, hipStream_t s) {
+  const zimg_dit_config& c = cfg;
+  const int D = c.hidden, P = c.patch * c.patch * c.in_channels;
+  int rc = prepare(L, t, s);
+  if (rc) return rc;
+  // patch embed -> image rows of x (fp32, bias)
+  HIP_TRY(zimg::launch_patchify(latent, xin, L.B, c.in_channels, L.Hp, L.Wp, c.patch, L.Npad, s));
+  zimg::GemmArgs ga{};
+  ga.A = xin;
+  ga.lda = P;
+  ga.W = x_w;
+  ga.ldw = P;
+  ga.M = L.B * L.Npad;
+  ga.N = D;
+  ga.K = P;
+  ga.epi = zimg::EPI_F32_BIAS;
+  ga.ep.C = x;
+  ga.ep.ldc = D;
+  ga.ep.bias = x_b;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+  // caption embed -> caption rows of x
+  int64_t src = 0;
+  for (int b = 0; b < L.B; ++b) {
+    const void* cb = cap_dtype == ZIMG_BF16 ? (const void*)((const uint16_t*)caps + src * c.cap_feat_dim)
+                                            : (const void*)((const float*)caps + src * c.cap_feat_dim);
+    HIP_TRY(zimg::launch_rows_rmsnorm(cb, cap_dtype == ZIMG_BF16, capn_w,
+                                      capn + (int64_t)(L.cap_off[b] - L.cap_base) * c.cap_feat_dim, L.lens[b],
+                                      c.cap_feat_dim, c.norm_eps, s));
+    src += L.lens[b];
+  }
+  ga.A = capn;
+  ga.lda = c.cap_feat_dim;
+  ga.W = cap_w;
+  ga.ldw = c.cap_feat_dim;
+  ga.M = L.S - L.cap_base;
+  ga.K = c.cap_feat_dim;
+  ga.ep.C = x + (int64_t)L.cap_base * D;
+  ga.ep.bias = cap_b;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+  const size_t slot_bytes = (size_t)L.S * D * 4;
+  if (cap_buf) HIP_TRY(hipMemcpyAsync(cap_buf, x, slot_bytes, hipMemcpyDeviceToDevice, s));
+
+  const int nb = (int)blocks.size();
+  bool h_ready = false;
+  bool final_ready = false;
+  for (int bi = 0; bi < nb; ++bi) {
+    int next = 0;
+    if (bi + 1 < nb && blocks[bi + 1].stage == blocks[bi].stage) next = 1;
+    else if (bi + 1 == nb && blocks[bi].stage != 1) next = 2;  // image rows are inside the block's rows
+    rc = run_block(bi, L, h_ready, next, s);
+    if (rc) return rc;
+    h_ready = next == 1;
+    final_ready = next == 2;
+    if (cap_buf) HIP_TRY(hipMemcpyAsync((char*)cap_buf + (size_t)(bi + 1) * slot_bytes, x, slot_bytes,
+                                        hipMemcpyDeviceToDevice, s));
+  }
+  if (!final_ready) {
+    zimg::PreNormArgs pa{x, nullptr, zimg::ModRef{mod, mod_stride, (int)(n_mod * 4 * D)}, row_sample, h, 0,
+                         L.cap_base, D, c.final_eps, 1};
+    HIP_TRY(zimg::launch_pre_norm(pa, s));
+  }
+  // final linear + unpatchify
+  ga = zimg::GemmArgs{};
+  ga.A = h;
+  ga.lda = D;
+  ga.W = fin_w;
+  ga.ldw = D;
+  ga.M = L.cap_base;
+  ga.N = P;
+  ga.K = D;
+  ga.epi = zimg::EPI_UNPATCH;
+  ga.ep.C = out;
+  ga.ep.bias = fin_b;
+  ga.ep.ntok = L.N;
+  ga.ep.npad = L.Npad;
+  ga.ep.Hp = L.Hp;
+  ga.ep.Wp = L.Wp;
+  ga.ep.C_ch = c.in_channels;
+  ga.ep.patch = c.patch;
+  HIP_TRY(zimg::launch_gemm(ga, s));
+  return ZIMG_OK;
+}
+
+int zimg_dit::run_blocks(float* x_io, const Layout& L, const float* t, int first, int n, hipStream_t s) {
+  int rc = prepare(L, t, s);
+  if (rc) return rc;
+  const size_t bytes = (size_t)L.S * cfg.hidden * 4;
+  HIP_TRY(hipMemcpyAsync(x, x_io, bytes, hipMemcpyDeviceToDevice, s));
+  bool h_ready = false;
+  for (int bi = first; bi < first + n; ++bi) {
+    const int next = (bi + 1 < first + n && blocks[bi + 1].stage == blocks[bi].stage) ? 1 : 0;
+    rc = run_block(bi, L, h_ready, next, s);
+    if (rc) return rc;
+    h_ready = next == 1;
+  }
+  HIP_TRY(hipMemcpyAsync(x_io, x, bytes, hipMemcpyDeviceToDevice, s));
+  return ZIMG_OK;
+}
+
+// ------------------------------------------------------------------ C ABI
+
+namespace {
+
+int validate_inputs(const zimg_dit* h, int32_t B, int32_t Hl, int32_t Wl, const int32_t* lens, const float* t) {
+  const zimg_dit_config& c = h->cfg;
+  if (!h->finalized) return set_err(ZIMG_ESTATE, "weights not finalized (missing zimg_dit_finalize?)");
+  if (B < 1 || B > c.max_batch) return set_err(ZIMG_EINVAL, "batch %d out of range 1..%d", B, c.max_batch);
+  if (Hl <= 0 || Wl <= 0 || Hl % c.patch || Wl % c.patch)
+    return set_err(ZIMG_EINVAL, "latent %dx%d: sides must be positive multiples of the patch size %d (image sides multiples of 16)",
+                   Hl, Wl, c.patch);
+  const int64_t ntok = (int64_t)(Hl / c.patch) * (Wl / c.patch);
+  if (ntok > c.max_image_tokens)
+    return set_err(ZIMG_EINVAL, "%lld image tokens exceed max_image_tokens %d", (long long)ntok, c.max_image_tokens);
+  if (!lens || !t) return set_err(ZIMG_EINVAL, "caption_lens and t must be host arrays, got NULL");
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < 1 || lens[b] > c.max_caption_tokens)
+      return set_err(ZIMG_EINVAL, "caption %d has length %d, outside 1..%d", b, lens[b], c.max_caption_tokens);
+    if (!std::isfinite(t[b])) return set_err(ZIMG_EINVAL, "t[%d] is not finite", b);
+  }
+  return ZIMG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zimg_last_error(void) { return g_last_error.c_str(); }
+
+void zimg_dit_default_config(zimg_dit_config* c) {
+  if (!c) return;
+  *c = zimg_dit_config{};
+  c->hidden = 3840;
+  c->n_heads = 30;
+  c->ffn = 10240;
+  c->n_layers = 30;
+  c->n_noise_refiner = 2;
+  c->n_context_refiner = 2;
+  c->in_channels = 16;
+  c->patch = 2;
+  c->cap_feat_dim = 2560;
+  c->adaln_dim = 256;
+  c->t_mid = 1024;
+  c->rope_axes[0] = 32;
+  c->rope_axes[1] = 48;
+  c->rope_axes[2] = 48;
+  c->rope_theta = 256.0f;
+  c->t_scale = 1000.0f;
+  c->max_period = 10000.0f;
+  c->norm_eps = 1e-5f;
+  c->final_eps = 1e-6f;
+  c->max_batch = 1;
+  c->max_image_tokens = 4096;
+  c->max_caption_tokens = 512;
+}
+
+int zimg_dit_check_config(const zimg_dit_config* cfg) {
+  g_last_error.clear();
+  return check_config(cfg);
+}
+
+int zimg_dit_manifest_size(const zimg_dit_config* cfg, int32_t* n) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!n) return set_err(ZIMG_EINVAL, "n_tensors is NULL");
+  *n = (int32_t)cached_manifest(*cfg).size();
+  return ZIMG_OK;
+}
+
+int zimg_dit_manifest_entry(const zimg_dit_config* cfg, int32_t index, const char** name, int32_t* ndim,
+                            int64_t shape[4]) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  const auto& m = cached_manifest(*cfg);
+  if (index < 0 || index >= (int32_t)m.size()) return set_err(ZIMG_EINVAL, "manifest index %d out of range", index);
+  if (name) *name = m[index].name.c_str();
+  if (ndim) *ndim = m[index].ndim;
+  if (shape)
+    for (int i = 0; i < 4; ++i) shape[i] = m[index].shape[i];
+  return ZIMG_OK;
+}
+
+int zimg_dit_alloc(const zimg_dit_config* cfg, zimg_dit** out) {
+  g_last_error.clear();
+  if (!out) return set_err(ZIMG_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev < 1)
+    return set_err(ZIMG_EHIP, "no HIP device available: %s", e != hipSuccess ? hipGetErrorString(e) : "0 devices");
+  std::unique_ptr<zimg_dit> h(new zimg_dit());
+  h->cfg = *cfg;
+  HIP_TRY(hipGetDevice(&h->device));
+  rc = h->allocate();
+  if (rc) return rc;
+  *out = h.release();
+  return ZIMG_OK;
+}
+
+int zimg_dit_set_weight(zimg_dit* h, const zimg_tensor* w) {
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  if (h->finalized) return h->fail(set_err(ZIMG_ESTATE, "weights already finalized"));
+  int rc = h->set_weight(w);
+  return rc ? h->fail(rc) : ZIMG_OK;
+}
+
+int zimg_dit_finalize(zimg_dit* h) {
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  int rc = h->finalize();
+  return rc ? h->fail(rc) : ZIMG_OK;
+}
+
+int zimg_dit_create(const zimg_dit_config* cfg, const zimg_tensor* weights, int32_t n_weights, zimg_dit** out) {
+  if (!out) return set_err(ZIMG_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (n_weights < 0 || (n_weights > 0 && !weights)) return set_err(ZIMG_EINVAL, "bad weights array");
+  zimg_dit* h = nullptr;
+  int rc = zimg_dit_alloc(cfg, &h);
+  if (rc) return rc;
+  for (int32_t i = 0; i < n_weights && !rc; ++i) rc = zimg_dit_set_weight(h, &weights[i]);
+  if (!rc) rc = zimg_dit_finalize(h);
+  if (rc) {
+    delete h;
+    return rc;
+  }
+  *out = h;
+  return ZIMG_OK;
+}
+
+void zimg_dit_destroy(zimg_dit* h) { delete h; }
+
+const char* zimg_dit_last_error(const zimg_dit* h) { return h ? h->err.c_str() : "handle is NULL"; }
+
+int zimg_dit_set_capture(zimg_dit* h, float* dev_buf, size_t bytes) {
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  h->cap_buf = dev_buf;
+  h->cap_bytes = dev_buf ? bytes : 0;
+  return ZIMG_OK;
+}
+
+int zimg_dit_forward(zimg_dit* h, const float* latent, int32_t B, int32_t Hl, int32_t Wl, const void* caption_feats,
+                     int32_t cap_dtype, const int32_t* caption_lens, const float* t, float* out, void* stream) {
+  g_last_error.clear();
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  int rc = validate_inputs(h, B, Hl, Wl, caption_lens, t);
+  if (rc) return h->fail(rc);
+  if (!latent || !caption_feats || !out) return h->fail(set_err(ZIMG_EINVAL, "latent, caption_feats and out must be non-NULL"));
+  if (cap_dtype != ZIMG_F32 && cap_dtype != ZIMG_BF16) return h->fail(set_err(ZIMG_EINVAL, "cap_dtype must be ZIMG_F32 or ZIMG_BF16"));
+  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
+  if (h->cap_buf) {
+    const size_t need = (size_t)(h->blocks.size() + 1) * L.S * h->cfg.hidden * 4;
+    if (h->cap_bytes < need) return h->fail(set_err(ZIMG_EINVAL, "capture buffer has %zu bytes, needs %zu", h->cap_bytes, need));
+  }
+  rc = h->forward(latent, L, caption_feats, cap_dtype, t, out, (hipStream_t)stream);
+  return rc ? h->fail(rc) : ZIMG_OK;
+}
+
+int zimg_dit_run_blocks(zimg_dit* h, float* x_io, int32_t B, int32_t Hl, int32_t Wl, const int32_t* caption_lens,
+                        const float* t, int32_t first_block, int32_t n_blocks, void* stream) {
+  g_last_error.clear();
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  int rc = validate_inputs(h, B, Hl, Wl, caption_lens, t);
+  if (rc) return h->fail(rc);
+  if (!x_io) return h->fail(set_err(ZIMG_EINVAL, "x_io is NULL"));
+  if (first_block < 0 || n_blocks < 1 || first_block + n_blocks > (int32_t)h->blocks.size())
+    return h->fail(set_err(ZIMG_EINVAL, "blocks [%d, %d) out of range 0..%zu", first_block, first_block + n_blocks,
+                           h->blocks.size()));
+  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
+  rc = h->run_blocks(x_io, L, t, first_block, n_blocks, (hipStream_t)stream);
+  return rc ? h->fail(rc) : ZIMG_OK;
+}
+
+int zimg_row_layout(int32_t B, int32_t n_image_tokens, const int32_t* caption_lens, int32_t* img_off, int32_t* cap_off,
+                    int32_t* S_total) {
+  g_last_error.clear();
+  if (B < 1 || n_image_tokens < 1 || !caption_lens) return set_err(ZIMG_EINVAL, "bad layout arguments");
+  for (int b = 0; b < B; ++b)
+    if (caption_lens[b] < 1) return set_err(ZIMG_EINVAL, "caption length must be >= 1");
+  const int64_t npad = round_up(n_image_tokens, 16);
+  int64_t off = (int64_t)B * npad;
+  for (int b = 0; b < B; ++b) {
+    if (img_off) img_off[b] = (int32_t)(b * npad);
+    if (cap_off) cap_off[b] = (int32_t)off;
+    off += round_up(caption_lens[b], 16);
+  }
+  if (S_total) *S_total = (int32_t)off;
+  return ZIMG_OK;
+}
+
+int zimg_position_ids(int32_t L, int32_t Hp, int32_t Wp, int32_t* cap_ids, int32_t* img_ids) {
+  g_last_error.clear();
+  if (L < 0 || Hp < 0 || Wp < 0 || (L && !cap_ids) || (Hp * Wp && !img_ids))
+    return set_err(ZIMG_EINVAL, "bad position-id arguments");
+  std::vector<int32_t> dummy(3);
+  position_ids(L, Hp, Wp, L ? cap_ids : dummy.data(), Hp * Wp ? img_ids : dummy.data());
+  return ZIMG_OK;
+}
+
+int zimg_rope_tables(const zimg_dit_config* cfg, const int32_t* ids, int64_t S, float* cs, float* sn) {
+  g_last_error.clear();
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (S < 0 || (S && (!ids || !cs || !sn))) return set_err(ZIMG_EINVAL, "bad rope-table arguments");
+  double omega[64];
+  int axis[64];
+  rope_freqs(*cfg, omega, axis);
+  rope_rows(omega, axis, ids, S, cs, sn);
+  return ZIMG_OK;
+}
+
+int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc, int32_t M, int32_t N,
+                   int32_t K, int32_t epilogue, const float* bias, void* stream) {
+  g_last_error.clear();
+  zimg::GemmArgs g{};
+  g.A = (const bf16_t*)A;
+  g.lda = lda;
+  g.W = (const bf16_t*)W;
+  g.ldw = ldw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.epi = epilogue;
+  g.ep.C = C;
+  g.ep.ldc = ldc;
+  g.ep.bias = bias;
+  if (epilogue == zimg::EPI_UNPATCH) return set_err(ZIMG_EUNSUPPORTED, "the unpatchify epilogue is internal");
+  if (const char* m = zimg::gemm_check(g)) return set_err(ZIMG_EINVAL, "%s", m);
+  const int64_t need = epilogue == zimg::EPI_SWIGLU ? N / 2 : N;
+  if (ldc < need) return set_err(ZIMG_EINVAL, "ldc %lld smaller than the output width %lld", (long long)ldc, (long long)need);
+  HIP_TRY(zimg::launch_gemm(g, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
+int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void* stream) {
+  g_last_error.clear();
+  if (!x || !model_out || n < 0) return set_err(ZIMG_EINVAL, "bad Euler-step arguments");
+  if (!std::isfinite(dt)) return set_err(ZIMG_EINVAL, "dt is not finite");
+  HIP_TRY(zimg::launch_euler(x, model_out, dt, n, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,142 @@
+// Launch interfaces of the gfx950 kernels (host side).  Every launcher
+// enqueues on the given stream and returns the launch status; argument
+// validation lives in the engine / C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace zimg {
+
+// ---------------------------------------------------------------- GEMM
+enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_SWIGLU = 2, EPI_UNPATCH = 3 };
+
+struct EpiArgs {
+  void* C;            // output base
+  int64_t ldc;        // row stride of C in elements (bf16 / f32 / swiglu)
+  const float* bias;  // [N] for F32_BIAS and UNPATCH (may be null)
+  // UNPATCH geometry: GEMM row = b*npad + n for token n = i*Wp + j of
+  // sample b (rows with n >= ntok are alignment padding and are skipped),
+  // GEMM column = (a*patch + b)*C_ch + ch; output [B, C_ch, Hp*patch, Wp*patch]
+  int ntok, npad, Hp, Wp, C_ch, patch;
+};
+
+struct GemmArgs {
+  const bf16_t* A;
+  int64_t lda;
+  const bf16_t* W;
+  int64_t ldw;
+  int M, N, K;
+  int epi;
+  EpiArgs ep;
+};
+
+const char* gemm_check(const GemmArgs& g);  // null if OK
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+
+// ---------------------------------------------------------------- norms
+// Modulation vectors: mod[sample * mod_stride + off + d], fp32.  A null
+// ``mod`` means unmodulated (scale 1, gate 1).
+struct ModRef {
+  const float* mod;
+  int64_t stride;
+  int off;
+};
+
+// h[r] = bf16( N(x[r]) * (1 + scale) ) for rows r in [r0, r1), with
+// N = RMSNorm with weight w (kind 0) or LayerNorm without affine (kind 1).
+struct PreNormArgs {
+  const float* x;
+  const float* w;
+  ModRef scale;
+  const int32_t* row_sample;
+  bf16_t* h;
+  int r0, r1, D;
+  float eps;
+  int kind;
+};
+hipError_t launch_pre_norm(const PreNormArgs& a, hipStream_t s);
+
+// For rows r in [r0, r1):  x[r] += gate * RMSNorm(y[r]; w_post), gate =
+// tanh(g) or 1; then, for rows in [n0, n1), h[r] = bf16(N_next(x[r]) * (1 + scale_next)).
+struct PostNormArgs {
+  float* x;
+  const bf16_t* y;
+  const float* w_post;
+  ModRef gate;
+  int r0, r1;
+  int n0, n1;  // n0 >= n1: no next norm
+  const float* w_next;
+  ModRef scale_next;
+  int next_kind;  // 0 RMSNorm, 1 LayerNorm (no affine)
+  float next_eps;
+  const int32_t* row_sample;
+  bf16_t* h;
+  int D;
+  float eps;
+};
+hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s);
+
+// Caption features (fp32 or bf16 rows of width Dc) -> bf16 RMSNorm(x; w).
+hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t* out,
+                               int rows, int Dc, float eps, hipStream_t s);
+
+// ---------------------------------------------------------------- QK norm + RoPE
+// qkv rows [r0, r1) of width 3*D: q and k heads RMS-normalised over 128
+// (weights wq, wk) and rotated by the row's table (cos/sin [S, 64]) in place;
+// v written transposed to vT[h][d][row] (row stride S_pad).
+struct QKRopeArgs {
+  bf16_t* qkv;
+  bf16_t* vT;
+  const float* wq;
+  const float* wk;
+  const float* cos_t;
+  const float* sin_t;
+  int r0, r1, H, S_pad;
+  float eps;
+};
+hipError_t launch_qknorm_rope(const QKRopeArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnSeg {
+  int r0[2];
+  int n[2];
+};
+struct AttnItem {
+  int q0;
+  int nq;
+  int seg;
+  int pad;
+};
+struct AttnArgs {
+  const bf16_t* qkv;
+  const bf16_t* vT;
+  bf16_t* out;
+  const AttnItem* items;
+  const AttnSeg* segs;
+  int n_items, H, S_pad;
+  float scale_log2;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- small ops
+// latent fp32 [B, C, Hp*p, Wp*p] -> tokens bf16, row b*npad + i*Wp + j, width p*p*C
+hipError_t launch_patchify(const float* latent, bf16_t* out, int B, int C, int Hp, int Wp,
+                           int patch, int npad, hipStream_t s);
+// e[b] = [cos(t_scale t_b f_i), sin(t_scale t_b f_i)], f_i = max_period^(-i/half)
+struct TimeArgs {
+  float t[64];
+};
+hipError_t launch_timestep_embed(const TimeArgs& t, int B, int dim, float t_scale,
+                                 float max_period, float* out, hipStream_t s);
+// y[b][n] = W[n] . act(x[b]) + bias[n]; act 0 = identity, 1 = SiLU.  K % 256 == 0.
+hipError_t launch_gemv(const bf16_t* W, const float* bias, const float* x, int64_t ldx,
+                       float* y, int64_t ldy, int N, int K, int B, int act, hipStream_t s);
+// x[i] += dt * (-o[i])
+hipError_t launch_euler(float* x, const float* o, float dt, int64_t n, hipStream_t s);
+// fill n floats with v
+hipError_t launch_fill(float* p, float v, int64_t n, hipStream_t s);
+
+}  // namespace zimg

@@ -1,0 +1,71 @@
+/*
+ * zimg_ops.h -- lower-level entry points of the S3-DiT engine: single
+ * blocks on a caller-supplied residual, the row layout of the sequence
+ * buffer, the bf16 projection GEMM, and the sampler's Euler update.
+ * Every pointer marked DEVICE is a HIP device pointer; every call is
+ * asynchronous on ``stream`` (a hipStream_t, NULL = default stream) and
+ * returns ZIMG_OK or a negative code (message: zimg_last_error()).
+ */
+#ifndef ZIMG_OPS_H
+#define ZIMG_OPS_H
+
+#include "zimg_dit.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Row layout of the single-stream sequence buffer the engine uses for B
+ * samples with n_image_tokens each and the given caption lengths ("Z-Image"
+ * (AI Toolkit docs), Architecture: text and image tokens share one
+ * sequence).  Image rows of sample b start at img_off[b] = b * Npad, Npad =
+ * n_image_tokens rounded up to 16; caption rows of sample b start at
+ * cap_off[b], after all image rows, each caption padded to a multiple of 16
+ * rows.  Padding rows belong to no sample.  S_total is the row count.
+ * Output arrays are HOST [B]; any output pointer may be NULL.
+ */
+int zimg_row_layout(int32_t B, int32_t n_image_tokens, const int32_t* caption_lens,
+                    int32_t* img_off, int32_t* cap_off, int32_t* S_total);
+
+/*
+ * Run blocks [first_block, first_block + n_blocks) of the model (execution
+ * order: noise refiners, context refiners, joint blocks) in place on the
+ * fp32 residual x_io (DEVICE [S_total, hidden], the row layout above), with
+ * the modulation of model time t (HOST [B]).  Each block touches the rows of
+ * its stage only: image rows (noise refiner), caption rows (context
+ * refiner) or all rows (joint).  Same argument rules as zimg_dit_forward.
+ */
+int zimg_dit_run_blocks(zimg_dit* h, float* x_io, int32_t B, int32_t Hl, int32_t Wl,
+                        const int32_t* caption_lens, const float* t, int32_t first_block,
+                        int32_t n_blocks, void* stream);
+
+/* Projection GEMM epilogues. */
+#define ZIMG_EPI_BF16 0     /* C bf16 [M, N] = A W^T */
+#define ZIMG_EPI_F32_BIAS 1 /* C fp32 [M, N] = A W^T + bias[N] (bias may be NULL) */
+#define ZIMG_EPI_SWIGLU 2   /* W rows interleaved in groups of 32 (32 rows of w1, then the
+                               same 32 rows of w3); C bf16 [M, N/2] = SiLU(h w1^T) * (h w3^T) */
+
+/*
+ * C = epilogue(A W^T): A DEVICE bf16 [M, K] (row stride lda), W DEVICE bf16
+ * [N, K] (row stride ldw; a linear layer's weight), C DEVICE with row
+ * stride ldc.  Constraints: K % 64 == 0, N % 64 == 0 (N % 256 for SwiGLU),
+ * lda, ldw multiples of 8.  fp32 accumulation on bf16 MFMA; no scratch.
+ */
+int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void* C, int64_t ldc,
+                   int32_t M, int32_t N, int32_t K, int32_t epilogue, const float* bias,
+                   void* stream);
+
+/*
+ * Euler update of the FlowMatch sampler: x[i] += dt * (-model_out[i]) for
+ * i < n ("Z-Image-Turbo MNN (int8, fp16-safe)", Scheduler: the model output
+ * is negated before the Euler step; dt = sigma'_{k+1} - sigma'_k).
+ * x, model_out DEVICE fp32.
+ */
+int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZIMG_OPS_H */

@@ -1,0 +1,203 @@
+"""Full-forward parity through the C ABI against the float64 oracle on the
+same seeded inputs: every block output (fp32 residual) and the final output,
+at the tiny single-block workload, the full-width single block at 512x512,
+and a small varlen batch whose image token count is not a multiple of 16.
+Also: bitwise determinism, bitwise batch independence, error paths."""
+
+import math
+
+import numpy as np
+import pytest
+
+import synthetic
+from oracle import model as om
+from tests import helpers
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _make_engine(model, max_batch, max_img, max_cap, seed=0, outlier_log2=None):
+    from diffusion_transformer_image_amd import binding
+    ecfg = helpers.engine_config(model, max_batch=max_batch, max_image_tokens=max_img,
+                                 max_caption_tokens=max_cap)
+    W = helpers.engine_weights(ecfg, seed=seed, outlier_log2=outlier_log2)
+    return binding.DiT(ecfg, W.items_parallel(as_bits=True))
+
+
+def _inputs(latent_shape, lens, seed=0):
+    torch = _torch()
+    lat = synthetic.latent(latent_shape, seed=seed)
+    caps = synthetic.captions(lens, seed=seed)
+    lat_d = torch.from_numpy(lat).cuda()
+    caps_d = torch.from_numpy(np.concatenate(caps)).cuda()
+    return lat, caps, lat_d, caps_d
+
+
+def _run_with_capture(dit, lat_d, caps_d, lens, t):
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    B, C, Hl, Wl = lat_d.shape
+    n_img = (Hl // 2) * (Wl // 2)
+    img_off, cap_off, S = binding.row_layout(B, n_img, lens)
+    D = dit.cfg.hidden
+    cap = torch.full(((dit.n_blocks + 1) * S * D,), float("nan"), device="cuda")
+    dit.set_capture(cap)
+    out = torch.empty_like(lat_d)
+    dit.forward(lat_d, caps_d, lens, t, out)
+    torch.cuda.synchronize()
+    dit.set_capture(None)
+    return out.cpu().numpy(), cap.cpu().numpy().reshape(dit.n_blocks + 1, S, D), img_off, cap_off
+
+
+def _compare_forward(model, wl_latent, lens, t, max_img, max_cap, seed=0):
+    dit = _make_engine(model, len(lens), max_img, max_cap, seed=seed)
+    lat, caps, lat_d, caps_d = _inputs(wl_latent, lens, seed=seed)
+    out, capt, img_off, cap_off = _run_with_capture(dit, lat_d, caps_d, lens, t)
+    ocfg = helpers.oracle_config(model)
+    Wo = helpers.oracle_weights(model, seed=seed)
+    from oracle.manifest import block_prefixes
+    prefixes = [p for p, _ in block_prefixes(ocfg)]
+    n_img = (wl_latent[2] // 2) * (wl_latent[3] // 2)
+    report = []
+    for b in range(len(lens)):
+        c = {}
+        ref = om.forward_sample(ocfg, Wo, lat[b], caps[b], float(np.float32(t[b])), capture=c)
+        ri = img_off[b] + np.arange(n_img)
+        rc = cap_off[b] + np.arange(lens[b])
+        helpers.assert_parity(capt[0][ri], c["x_embed"], f"sample {b} x_embed")
+        helpers.assert_parity(capt[0][rc], c["cap_embed"], f"sample {b} cap_embed")
+        # block inputs of each side: the branch check subtracts each side's own input
+        o_img, o_cap = c["x_embed"], c["cap_embed"]
+        g_img, g_cap = capt[0][ri], capt[0][rc]
+        o_prev = g_prev = None
+        for i, p in enumerate(prefixes):
+            slot = capt[i + 1]
+            if p.startswith("noise_refiner"):
+                got, want, gin, oin = slot[ri], c[p], g_img, o_img
+                g_img, o_img = got, want
+            elif p.startswith("context_refiner"):
+                got, want, gin, oin = slot[rc], c[p], g_cap, o_cap
+                g_cap, o_cap = got, want
+            else:
+                got, want = np.concatenate([slot[ri], slot[rc]]), c[p]
+                if o_prev is None:
+                    gin, oin = np.concatenate([g_img, g_cap]), np.concatenate([o_img, o_cap])
+                else:
+                    gin, oin = g_prev, o_prev
+                g_prev, o_prev = got, want
+            r, cs = helpers.assert_parity(got, want, f"sample {b} {p}")
+            # what the block added, compared on its own (not diluted by the residual)
+            rb = helpers.rel_l2(got - gin, want - oin)
+            assert rb <= 3e-2, f"sample {b} {p}: branch rel-L2 {rb:.3e}"
+            report.append((b, p, r, cs, rb))
+        helpers.assert_parity(out[b], ref, f"sample {b} final output")
+    return report, dit
+
+
+def test_forward_tiny_block():
+    wl = synthetic.WORKLOADS["tiny_block"]
+    rep, _ = _compare_forward(wl["model"], wl["latent"], wl["caption_lens"], wl["t"], 256, 32)
+    print(rep)
+
+
+def test_forward_block_512():
+    wl = synthetic.WORKLOADS["block_512"]
+    rep, _ = _compare_forward(wl["model"], wl["latent"], wl["caption_lens"], wl["t"], 1024, 128)
+    print(rep)
+
+
+SMALL = dict(hidden=512, n_heads=4, ffn=1536, n_layers=2, n_noise_refiner=1, n_context_refiner=1)
+
+
+def test_forward_small_varlen_batch():
+    """B = 2, captions 77 and 45 tokens, 12x10 = 120 image tokens (padded rows)."""
+    rep, _ = _compare_forward(SMALL, (2, 16, 24, 20), (77, 45), (0.3, 0.8), 120, 77)
+    print(rep)
+
+
+def test_determinism_and_batch_independence():
+    torch = _torch()
+    dit = _make_engine(SMALL, 2, 120, 77, seed=3)
+    lens = (77, 45)
+    lat, caps, lat_d, caps_d = _inputs((2, 16, 24, 20), lens, seed=3)
+    t = (0.3, 0.8)
+    o1 = torch.empty_like(lat_d)
+    o2 = torch.empty_like(lat_d)
+    dit.forward(lat_d, caps_d, lens, t, o1)
+    dit.forward(lat_d, caps_d, lens, t, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    for b in range(2):
+        ob = torch.empty_like(lat_d[b:b + 1])
+        dit.forward(lat_d[b:b + 1].contiguous(), torch.from_numpy(caps[b]).cuda(), lens[b:b + 1], t[b:b + 1], ob)
+        torch.cuda.synchronize()
+        assert torch.equal(ob[0], o1[b]), f"sample {b} differs when run alone"
+
+
+def test_caption_bf16_input_matches_fp32():
+    torch = _torch()
+    dit = _make_engine(SMALL, 1, 120, 77, seed=4)
+    lat, caps, lat_d, caps_d = _inputs((1, 16, 24, 20), (50,), seed=4)
+    o1 = torch.empty_like(lat_d)
+    o2 = torch.empty_like(lat_d)
+    dit.forward(lat_d, caps_d, (50,), (0.5,), o1)
+    dit.forward(lat_d, caps_d.to(torch.bfloat16), (50,), (0.5,), o2)  # captions are bf16-exact
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_forward_argument_errors():
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    dit = _make_engine(SMALL, 1, 120, 77, seed=5)
+    lat_d = torch.zeros((1, 16, 24, 20), device="cuda")
+    caps_d = torch.zeros((50, 2560), device="cuda")
+    out = torch.empty_like(lat_d)
+    bad = [
+        (lambda: dit.forward(torch.zeros((1, 16, 23, 20), device="cuda"), caps_d, (50,), (0.5,), out), "multiples"),
+        (lambda: dit.forward(lat_d, caps_d, (0,), (0.5,), out), "length 0"),
+        (lambda: dit.forward(lat_d, caps_d, (78,), (0.5,), out), "outside 1..77"),
+        (lambda: dit.forward(lat_d, caps_d, (50,), (math.nan,), out), "not finite"),
+        (lambda: dit.forward(torch.zeros((1, 16, 24, 22), device="cuda"), caps_d, (50,), (0.5,), out), "exceed"),
+        (lambda: dit.forward(torch.zeros((2, 16, 24, 20), device="cuda"), caps_d, (50, 50), (0.5, 0.5), out), "batch"),
+    ]
+    for fn, msg in bad:
+        with pytest.raises(binding.ZimgError) as ei:
+            fn()
+        assert ei.value.code == binding.ZIMG_EINVAL and msg in str(ei.value), str(ei.value)
+
+
+def test_weight_table_errors():
+    _torch()
+    from diffusion_transformer_image_amd import binding
+    model = synthetic.WORKLOADS["tiny_block"]["model"]
+    ecfg = helpers.engine_config(model, 1, 256, 32)
+    W = dict(helpers.engine_weights(ecfg).materialize(workers=4))
+    names = list(W)
+    # missing
+    with pytest.raises(binding.ZimgError) as ei:
+        binding.DiT(ecfg, [(n, W[n]) for n in names[:-1]])
+    assert ei.value.code == binding.ZIMG_EWEIGHT and names[-1] in str(ei.value)
+    # unknown
+    with pytest.raises(binding.ZimgError) as ei:
+        binding.DiT(ecfg, list(W.items()) + [("layers.0.attention.to_qkv.weight", W[names[0]])])
+    assert ei.value.code == binding.ZIMG_EWEIGHT and "unknown" in str(ei.value)
+    # duplicate
+    with pytest.raises(binding.ZimgError) as ei:
+        binding.DiT(ecfg, list(W.items()) + [(names[3], W[names[3]])])
+    assert ei.value.code == binding.ZIMG_EWEIGHT and "duplicate" in str(ei.value)
+    # mis-shaped
+    bad = dict(W)
+    bad["x_embedder.weight"] = W["x_embedder.weight"][:, :32].copy()
+    with pytest.raises(binding.ZimgError) as ei:
+        binding.DiT(ecfg, bad)
+    assert ei.value.code == binding.ZIMG_EWEIGHT and "x_embedder.weight" in str(ei.value)
+    # fp32 and bf16-bit inputs give the same engine
+    binding.DiT(ecfg, W).close()
