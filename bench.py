@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Throughput of the Z-Image S3-DiT denoiser forward on one MI355X.
+
+A step is one full forward (patch + caption embeds, 2 noise-refiner, 2
+context-refiner and 30 joint blocks, final layer) of the 1024x1024 workload:
+latent [1, 16, 128, 128] (4,096 image tokens) and a 512-token caption, with
+random-init bf16 weights of the full 6.15B-parameter model and N(0, 1)
+synthetic inputs, all resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: tokens/s of the whole job, ms per step, the bf16 MFMA
+utilisation end to end, the roofline of the dominant kernel (timed live with
+HIP events on the engine's stream) and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT forward tokens/sec at 1024^2 (4096+512 tok), 1 MI355X; MFMA util %"
+PEAK_BF16 = 2.5e15  # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12   # bytes/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def stage_rows(model, n_img, lens):
+    """Rows (tokens) each block of the stack processes, per sample, in order."""
+    out = []
+    for _ in range(model["n_noise_refiner"]):
+        out.append(("noise", [n_img for _ in lens]))
+    for _ in range(model["n_context_refiner"]):
+        out.append(("context", list(lens)))
+    for _ in range(model["n_layers"]):
+        out.append(("joint", [n_img + L for L in lens]))
+    return out
+
+
+def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
+    """Algorithmic FLOPs of the MFMA classes and algorithmic HBM bytes of the
+    bandwidth-bound classes, per forward, keyed by the engine's profile classes."""
+    D, F = model["hidden"], model["ffn"]
+    w = {k: 0.0 for k in ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
+                          "qknorm_rope", "pre_norm", "post_norm", "embed", "final_layer", "conditioning")}
+    stages = stage_rows(model, n_img, lens)
+    prev = None
+    for i, (stage, rows) in enumerate(stages):
+        M = sum(rows)
+        w["gemm_qkv"] += 2.0 * M * D * 3 * D
+        w["gemm_out"] += 2.0 * M * D * D
+        w["gemm_w13_swiglu"] += 2.0 * M * D * 2 * F
+        w["gemm_w2"] += 2.0 * M * F * D
+        w["attention"] += sum(4.0 * r * r * D for r in rows)
+        # bytes: q,k read+write, v read + transposed write (bf16), RoPE tables (fp32 cos+sin)
+        w["qknorm_rope"] += M * (12.0 * D + 512)
+        # pre-norm only where not fused into the previous block's last kernel
+        if prev != stage:
+            w["pre_norm"] += M * 6.0 * D
+        # two post-norms: read y bf16, read+write x fp32, write next h bf16 (12 B/elem);
+        # the last one of a stage without a fused follow-up skips the h write (10 B/elem)
+        nxt = stages[i + 1][0] if i + 1 < len(stages) else "final"
+        w["post_norm"] += M * 12.0 * D + M * (12.0 if (nxt == stage or nxt == "final") else 10.0) * D
+        prev = stage
+    T = sum(lens)
+    w["embed"] = 2.0 * n_img * len(lens) * patch_dim * D + 2.0 * T * cap_dim * D
+    w["final_layer"] = 2.0 * n_img * len(lens) * D * patch_dim
+    n_mod = model["n_noise_refiner"] + model["n_layers"]
+    w["conditioning"] = 2.0 * (n_mod * 4 * D + D) * adaln  # the GEMVs: bytes ~ flops (bf16 weights)
+    return w
+
+
+MFMA_CLASSES = ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention", "embed", "final_layer")
+HBM_CLASSES = ("qknorm_rope", "pre_norm", "post_norm")
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(wl, model):
+    """Time the float64 oracle on one joint block of the workload (all rows),
+    then scale to a whole forward by the algorithmic FLOP ratio."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synthetic
+    from oracle import ModelConfig, manifest
+    from oracle import model as om
+
+    cfg = ModelConfig.from_dict(model)
+    lat_shape, lens = wl["latent"], wl["caption_lens"]
+    Hp, Wp = lat_shape[2] // 2, lat_shape[3] // 2
+    n_img, L = Hp * Wp, lens[0]
+    S = n_img + L
+    W = synthetic.SyntheticWeights(manifest(cfg), seed=wl["seed"])
+    p = "layers.0"
+    need = [n for n, _ in manifest(cfg) if n.startswith(p + ".") or n.startswith("t_embedder.")]
+    Wb = {n: W[n] for n in need}
+    x = synthetic.residual((S, cfg.hidden), seed=wl["seed"]).astype(np.float64)
+    cap_ids, img_ids = om.position_ids(L, Hp, Wp)
+    cos, sin = om.rope_tables(cfg, np.concatenate([img_ids, cap_ids]))
+    c = om.timestep_mlp(cfg, Wb, np.array([wl["t"][0]]))[0]
+    mod = om.block_modulation(Wb, p, c)
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    om.block(cfg, Wb, p, x, cos, sin, mod)
+    block_s = time.perf_counter() - t0
+    w = work_per_forward(model, n_img, lens)
+    fwd_flops = sum(w[k] for k in MFMA_CLASSES)
+    Dm, Fm = model["hidden"], model["ffn"]
+    joint_flops = 2.0 * S * Dm * (4 * Dm + 3 * Fm) + 4.0 * S * S * Dm
+    fwd_s = block_s * fwd_flops / joint_flops
+    return {"value": round(S / fwd_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"one joint block (all {S} rows, hidden {Dm}) of the forward in float64 numpy, "
+                       f"{block_s:.2f} s; whole-forward time scaled by algorithmic FLOPs "
+                       f"({fwd_flops / joint_flops:.2f} x the block)")}
+
+
+# ---------------------------------------------------------------- traffic from committed counters
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "attention.hip", "norm.hip", "common.h"):
+        with open(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", txt)
+    if not m or not d or d.group(1) != source_digest():
+        return None
+    return float(m.group(1))
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dit_1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also launch one plain device copy of this many MiB (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py: this engine runs on one GPU; --gpus {args.gpus} is not supported "
+              "(data-parallel sharding over samples needs no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic
+    from diffusion_transformer_image_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        log("library not built; building it")
+        from diffusion_transformer_image_amd import build as _b
+        _b.build(verbose=False)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synthetic.WORKLOADS[args.workload]
+    model = wl["model"]
+    lat_shape, lens = wl["latent"], list(wl["caption_lens"])
+    B = lat_shape[0]
+    n_img = (lat_shape[2] // 2) * (lat_shape[3] // 2)
+    tokens = B * n_img + sum(lens)
+    t = list(wl["t"]) if wl.get("t") else [0.5] * B
+
+    cfg = binding.config(max_batch=B, max_image_tokens=n_img, max_caption_tokens=max(lens), **model)
+    W = synthetic.SyntheticWeights(binding.manifest(cfg), seed=wl["seed"], outlier_log2=wl.get("outlier_log2"))
+    t0 = time.perf_counter()
+    log(f"drawing and uploading {len(W)} weight tensors ({args.workload})")
+    dit = binding.DiT(cfg, W.items_parallel(as_bits=True))
+    log(f"engine ready in {time.perf_counter() - t0:.1f} s")
+    lat = torch.from_numpy(synthetic.latent(lat_shape, seed=wl["seed"])).cuda()
+    caps = torch.from_numpy(np.concatenate(synthetic.captions(lens, seed=wl["seed"]))).cuda()
+    out = torch.empty_like(lat)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        dit.forward(lat, caps, lens, t, out)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: K whole forwards
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        dit.forward(lat, caps, lens, t, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    gpu_ms = e0.elapsed_time(e1)
+    log(f"timed {args.steps} steps: wall {wall * 1e3:.1f} ms, events {gpu_ms:.1f} ms")
+    assert torch.isfinite(out).all().item(), "non-finite output"
+
+    # per-kernel timing: the same K forwards with event brackets around each kernel class
+    dit.profile(True)
+    for _ in range(args.steps):
+        dit.forward(lat, caps, lens, t, out)
+    torch.cuda.synchronize()
+    stats = dit.profile_read()
+    dit.profile(False)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration} MiB read + written")
+
+    work = work_per_forward(model, n_img, lens)
+    kernels = {}
+    for name, (launches, ms) in stats.items():
+        if launches == 0:
+            continue
+        per_fwd_ms = ms / args.steps
+        entry = {"ms_per_forward": round(per_fwd_ms, 4), "launches_per_forward": launches // args.steps,
+                 "avg_launch_us": round(ms / launches * 1e3, 2)}
+        if name in MFMA_CLASSES:
+            ach = work[name] / (per_fwd_ms * 1e-3)
+            entry.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / PEAK_BF16, 4))
+        elif name in HBM_CLASSES:
+            ach = work[name] / (per_fwd_ms * 1e-3)
+            entry.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / PEAK_HBM, 4))
+        kernels[name] = entry
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_forward"])
+    d = kernels[dom]
+    launches_dom = stats[dom][0] / args.steps
+    per_launch = work[dom] / launches_dom if launches_dom else 0.0
+    avg_s = d["avg_launch_us"] * 1e-6
+    if dom in HBM_CLASSES:
+        roof = {"bound": "hbm", "achieved": round(per_launch / avg_s / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(per_launch / avg_s / 1e12, 2), "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = committed_traffic(dom, args.workload)
+    roof["kernel"] = dom
+    roof["work_per_launch"] = per_launch
+
+    ms_per_step = wall * 1e3 / args.steps
+    fwd_flops = sum(work[k] for k in MFMA_CLASSES)
+    result = {
+        "metric": METRIC,
+        "value": round(tokens * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "latent": list(lat_shape), "caption_tokens": lens,
+                   "tokens_per_forward": tokens, "blocks": len(stage_rows(model, n_img, lens)),
+                   "t": t},
+        "mfma_util_pct": round(100.0 * fwd_flops / (ms_per_step * 1e-3) / PEAK_BF16, 2),
+        "algorithmic_tflop_per_forward": round(fwd_flops / 1e12, 3),
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, model) if B == 1 else None
+    dit.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,10 @@ class Config(ctypes.Structure):
         return d
 
 
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
 class Tensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 4)]
@@ -88,6 +92,8 @@ SIGNATURES = {
     "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
     "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
+    "zimg_dit_profile": (_I32, [_P, _I32]),
+    "zimg_dit_profile_read": (_I32, [_P, ctypes.POINTER(KernelStat), _I32, _I32P]),
 }
 
 _lib = None
@@ -233,6 +239,17 @@ class DiT:
         _check(lib().zimg_dit_run_blocks(self._h, _ptr(x), B, Hl, Wl, lens.ctypes.data_as(_I32P),
                                          tt.ctypes.data_as(_F32P), first, n, _stream(stream)), self._h)
         return x
+
+    def profile(self, enable):
+        """Start (reset) or stop per-kernel-class event timing."""
+        _check(lib().zimg_dit_profile(self._h, 1 if enable else 0), self._h)
+
+    def profile_read(self):
+        """{class name: (launches, total_ms)} accumulated since profile(True)."""
+        stats = (KernelStat * 32)()
+        n = ctypes.c_int32()
+        _check(lib().zimg_dit_profile_read(self._h, stats, 32, ctypes.byref(n)), self._h)
+        return {stats[i].name.decode(): (stats[i].launches, stats[i].total_ms) for i in range(min(n.value, 32))}
 
     def set_capture(self, buf):
         """buf: torch CUDA fp32 tensor or None."""

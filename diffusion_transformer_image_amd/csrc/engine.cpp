@@ -51,6 +51,16 @@ int set_err(int code, const char* fmt, ...) {
       return set_err(ZIMG_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));        \
   } while (0)
 
+// run ``call`` (a hipError_t expression) bracketed by the profiler's events
+#define PROFILED(cls, call)                          \
+  do {                                               \
+    int prc_ = prof_start(cls, s);                   \
+    if (prc_) return prc_;                           \
+    HIP_TRY(call);                                   \
+    prc_ = prof_stop(s);                             \
+    if (prc_) return prc_;                           \
+  } while (0)
+
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 uint16_t f32_to_bf16(float f) {
@@ -313,6 +323,44 @@ struct zimg_dit {
 
   std::vector<void*> allocations;
 
+  // per-kernel-class timing with HIP events on the forward's stream
+  enum { K_QKV, K_OUT, K_W13, K_W2, K_ATTN, K_QKROPE, K_PRENORM, K_POSTNORM, K_EMBED, K_FINAL, K_COND, K_COUNT };
+  struct Prof {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // pairs (start, stop)
+    std::vector<int> cls;
+    size_t used = 0;
+    int64_t count[K_COUNT] = {};
+    double ms[K_COUNT] = {};
+  } prof;
+  int prof_harvest() {
+    for (size_t i = 0; i < prof.used; ++i) {
+      HIP_TRY(hipEventSynchronize(prof.ev[2 * i + 1]));
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, prof.ev[2 * i], prof.ev[2 * i + 1]));
+      prof.count[prof.cls[i]] += 1;
+      prof.ms[prof.cls[i]] += ms;
+    }
+    prof.used = 0;
+    return ZIMG_OK;
+  }
+  int prof_start(int c, hipStream_t s) {
+    if (!prof.on) return ZIMG_OK;
+    if (prof.used == prof.cls.size()) {
+      int rc = prof_harvest();
+      if (rc) return rc;
+    }
+    prof.cls[prof.used] = c;
+    HIP_TRY(hipEventRecord(prof.ev[2 * prof.used], s));
+    return ZIMG_OK;
+  }
+  int prof_stop(hipStream_t s) {
+    if (!prof.on) return ZIMG_OK;
+    HIP_TRY(hipEventRecord(prof.ev[2 * prof.used + 1], s));
+    prof.used += 1;
+    return ZIMG_OK;
+  }
+
   int fail(int code) {
     err = g_last_error;
     return code;
@@ -333,6 +381,7 @@ struct zimg_dit {
   }
 
   ~zimg_dit() {
+    for (hipEvent_t e : prof.ev) (void)hipEventDestroy(e);
     for (void* p : allocations) (void)hipFree(p);
     if (staging) (void)hipHostFree(staging);
     if (staging_done) (void)hipEventDestroy(staging_done);
@@ -591,16 +640,18 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
   // timestep embedding -> MLP -> every modulation vector
   zimg::TimeArgs ta{};
   for (int b = 0; b < L.B; ++b) ta.t[b] = t[b];
+  const int64_t D = c.hidden;
+  int rc = prof_start(K_COND, s);
+  if (rc) return rc;
   HIP_TRY(zimg::launch_timestep_embed(ta, L.B, c.adaln_dim, c.t_scale, c.max_period, temb, s));
   HIP_TRY(zimg::launch_gemv(t1w, t1b, temb, c.adaln_dim, hmid, c.t_mid, c.t_mid, c.adaln_dim, L.B, 0, s));
   HIP_TRY(zimg::launch_gemv(t2w, t2b, hmid, c.t_mid, cvec, c.adaln_dim, c.adaln_dim, c.t_mid, L.B, 1, s));
-  const int64_t D = c.hidden;
   if (n_mod)
     HIP_TRY(zimg::launch_gemv(ada_w, ada_b, cvec, c.adaln_dim, mod, mod_stride, (int)(n_mod * 4 * D), c.adaln_dim,
                               L.B, 0, s));
   HIP_TRY(zimg::launch_gemv(ada_w + n_mod * 4 * D * c.adaln_dim, ada_b + n_mod * 4 * D, cvec, c.adaln_dim,
                             mod + n_mod * 4 * D, mod_stride, (int)D, c.adaln_dim, L.B, 1, s));
-  return ZIMG_OK;
+  return prof_stop(s);
 }
 
 static void stage_rows(const Layout& L, int stage, int& r0, int& r1) {
@@ -626,7 +677,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   };
   if (!h_ready) {
     zimg::PreNormArgs pa{x, w.an1, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0};
-    HIP_TRY(zimg::launch_pre_norm(pa, s));
+    PROFILED(K_PRENORM, zimg::launch_pre_norm(pa, s));
   }
   zimg::GemmArgs ga{};
   ga.A = h + (int64_t)r0 * D;
@@ -639,21 +690,23 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.epi = zimg::EPI_BF16;
   ga.ep.C = qkv + (int64_t)r0 * 3 * D;
   ga.ep.ldc = 3 * D;
-  HIP_TRY(zimg::launch_gemm(ga, s));
+  ga.role = zimg::ROLE_QKV;
+  PROFILED(K_QKV, zimg::launch_gemm(ga, s));
 
   zimg::QKRopeArgs qa{qkv, vT, w.nq, w.nk, cos_t, sin_t, r0, r1, H, (int)S_pad, c.norm_eps};
-  HIP_TRY(zimg::launch_qknorm_rope(qa, s));
+  PROFILED(K_QKROPE, zimg::launch_qknorm_rope(qa, s));
 
   zimg::AttnArgs aa{qkv, vT, o, items + stage * max_items, segs + stage * c.max_batch, n_items_stage[stage], H,
                     (int)S_pad, (float)(1.4426950408889634 / std::sqrt(128.0))};
-  HIP_TRY(zimg::launch_attention(aa, s));
+  PROFILED(K_ATTN, zimg::launch_attention(aa, s));
 
   ga.A = o + (int64_t)r0 * D;
   ga.W = w.wo;
   ga.N = D;
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
-  HIP_TRY(zimg::launch_gemm(ga, s));
+  ga.role = zimg::ROLE_OUT;
+  PROFILED(K_OUT, zimg::launch_gemm(ga, s));
 
   zimg::PostNormArgs pn{};
   pn.x = x;
@@ -672,7 +725,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   pn.h = h;
   pn.D = D;
   pn.eps = c.norm_eps;
-  HIP_TRY(zimg::launch_post_norm(pn, s));
+  PROFILED(K_POSTNORM, zimg::launch_post_norm(pn, s));
 
   ga.A = h + (int64_t)r0 * D;
   ga.W = w.w13;
@@ -680,7 +733,8 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.epi = zimg::EPI_SWIGLU;
   ga.ep.C = g + (int64_t)r0 * F;
   ga.ep.ldc = F;
-  HIP_TRY(zimg::launch_gemm(ga, s));
+  ga.role = zimg::ROLE_W13;
+  PROFILED(K_W13, zimg::launch_gemm(ga, s));
 
   ga.A = g + (int64_t)r0 * F;
   ga.lda = F;
@@ -691,7 +745,8 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.epi = zimg::EPI_BF16;
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
-  HIP_TRY(zimg::launch_gemm(ga, s));
+  ga.role = zimg::ROLE_W2;
+  PROFILED(K_W2, zimg::launch_gemm(ga, s));
 
   pn.w_post = w.fn2;
   pn.gate = mref(3);
@@ -712,7 +767,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   } else {
     pn.n0 = pn.n1 = 0;
   }
-  HIP_TRY(zimg::launch_post_norm(pn, s));
+  PROFILED(K_POSTNORM, zimg::launch_post_norm(pn, s));
   return ZIMG_OK;
 }
 
@@ -722,7 +777,9 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   const int D = c.hidden, P = c.patch * c.patch * c.in_channels;
   int rc = prepare(L, t, s);
   if (rc) return rc;
-  // patch embed -> image rows of x (fp32, bias)
+  // patch embed -> image rows of x (fp32, bias); caption embed -> caption rows
+  rc = prof_start(K_EMBED, s);
+  if (rc) return rc;
   HIP_TRY(zimg::launch_patchify(latent, xin, L.B, c.in_channels, L.Hp, L.Wp, c.patch, L.Npad, s));
   zimg::GemmArgs ga{};
   ga.A = xin;
@@ -733,11 +790,11 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.N = D;
   ga.K = P;
   ga.epi = zimg::EPI_F32_BIAS;
+  ga.role = zimg::ROLE_EMBED;
   ga.ep.C = x;
   ga.ep.ldc = D;
   ga.ep.bias = x_b;
   HIP_TRY(zimg::launch_gemm(ga, s));
-  // caption embed -> caption rows of x
   int64_t src = 0;
   for (int b = 0; b < L.B; ++b) {
     const void* cb = cap_dtype == ZIMG_BF16 ? (const void*)((const uint16_t*)caps + src * c.cap_feat_dim)
@@ -756,6 +813,8 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.ep.C = x + (int64_t)L.cap_base * D;
   ga.ep.bias = cap_b;
   HIP_TRY(zimg::launch_gemm(ga, s));
+  rc = prof_stop(s);
+  if (rc) return rc;
   const size_t slot_bytes = (size_t)L.S * D * 4;
   if (cap_buf) HIP_TRY(hipMemcpyAsync(cap_buf, x, slot_bytes, hipMemcpyDeviceToDevice, s));
 
@@ -773,6 +832,8 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
     if (cap_buf) HIP_TRY(hipMemcpyAsync((char*)cap_buf + (size_t)(bi + 1) * slot_bytes, x, slot_bytes,
                                         hipMemcpyDeviceToDevice, s));
   }
+  rc = prof_start(K_FINAL, s);
+  if (rc) return rc;
   if (!final_ready) {
     zimg::PreNormArgs pa{x, nullptr, zimg::ModRef{mod, mod_stride, (int)(n_mod * 4 * D)}, row_sample, h, 0,
                          L.cap_base, D, c.final_eps, 1};
@@ -788,6 +849,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.N = P;
   ga.K = D;
   ga.epi = zimg::EPI_UNPATCH;
+  ga.role = zimg::ROLE_FINAL;
   ga.ep.C = out;
   ga.ep.bias = fin_b;
   ga.ep.ntok = L.N;
@@ -797,7 +859,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.ep.C_ch = c.in_channels;
   ga.ep.patch = c.patch;
   HIP_TRY(zimg::launch_gemm(ga, s));
-  return ZIMG_OK;
+  return prof_stop(s);
 }
 
 int zimg_dit::run_blocks(float* x_io, const Layout& L, const float* t, int first, int n, hipStream_t s) {
@@ -1043,11 +1105,53 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
   g.ep.C = C;
   g.ep.ldc = ldc;
   g.ep.bias = bias;
+  g.role = zimg::ROLE_ANY;
   if (epilogue == zimg::EPI_UNPATCH) return set_err(ZIMG_EUNSUPPORTED, "the unpatchify epilogue is internal");
   if (const char* m = zimg::gemm_check(g)) return set_err(ZIMG_EINVAL, "%s", m);
   const int64_t need = epilogue == zimg::EPI_SWIGLU ? N / 2 : N;
   if (ldc < need) return set_err(ZIMG_EINVAL, "ldc %lld smaller than the output width %lld", (long long)ldc, (long long)need);
   HIP_TRY(zimg::launch_gemm(g, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
+int zimg_dit_profile(zimg_dit* h, int32_t enable) {
+  g_last_error.clear();
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  if (enable) {
+    if (h->prof.ev.empty()) {
+      const size_t pairs = 4096;
+      h->prof.ev.resize(2 * pairs, nullptr);
+      h->prof.cls.resize(pairs, 0);
+      for (auto& e : h->prof.ev) {
+        hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return h->fail(set_err(ZIMG_EHIP, "hipEventCreate failed: %s", hipGetErrorString(err)));
+      }
+    }
+    h->prof.used = 0;
+    for (int i = 0; i < zimg_dit::K_COUNT; ++i) {
+      h->prof.count[i] = 0;
+      h->prof.ms[i] = 0.0;
+    }
+  }
+  h->prof.on = enable != 0;
+  return ZIMG_OK;
+}
+
+int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats) {
+  static const char* names[zimg_dit::K_COUNT] = {"gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
+                                                 "qknorm_rope", "pre_norm", "post_norm", "embed", "final_layer",
+                                                 "conditioning"};
+  g_last_error.clear();
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  if (max_stats < 0 || (max_stats > 0 && !stats)) return set_err(ZIMG_EINVAL, "bad stats array");
+  int rc = h->prof_harvest();
+  if (rc) return h->fail(rc);
+  for (int i = 0; i < zimg_dit::K_COUNT && i < max_stats; ++i) {
+    stats[i].name = names[i];
+    stats[i].launches = h->prof.count[i];
+    stats[i].total_ms = h->prof.ms[i];
+  }
+  if (n_stats) *n_stats = zimg_dit::K_COUNT;
   return ZIMG_OK;
 }
 

@@ -29,7 +29,9 @@ constexpr int BK = 64;
 constexpr int NT = 512;
 constexpr int GROUP_M = 8;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// ROLE only separates the symbols of the projections (qkv, out, w1|w3, w2,
+// embeds, final) so that profiles attribute time per projection.
+template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
 __global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                   const bf16_t* __restrict__ W, int64_t ldw,
                                                   int M, int N, int K, EpiArgs ep, int tiles_m,
@@ -186,19 +188,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI>), dim3(tiles_m * tiles_n), dim3(NT), 0, s,
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE>), dim3(tiles_m * tiles_n), dim3(NT), 0, s,
                      g.A, g.lda, g.W, g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
-template <int EPI>
+template <int EPI, int ROLE>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
-  if (g.N % 256 == 0) return launch_cfg<256, 256, 2, 4, EPI>(g, s);
-  if (g.N % 128 == 0) return launch_cfg<256, 128, 4, 2, EPI>(g, s);
-  return launch_cfg<256, 64, 8, 1, EPI>(g, s);
+  if (g.N % 256 == 0) return launch_cfg<256, 256, 2, 4, EPI, ROLE>(g, s);
+  if (g.N % 128 == 0) return launch_cfg<256, 128, 4, 2, EPI, ROLE>(g, s);
+  return launch_cfg<256, 64, 8, 1, EPI, ROLE>(g, s);
 }
 
 }  // namespace
@@ -214,15 +216,28 @@ const char* gemm_check(const GemmArgs& g) {
   if (g.epi == EPI_UNPATCH && (g.ep.ntok <= 0 || g.ep.npad < g.ep.ntok || g.ep.Wp <= 0 || g.ep.C_ch <= 0 || g.ep.patch <= 0))
     return "gemm: bad unpatchify geometry";
   if (g.epi < 0 || g.epi > EPI_UNPATCH) return "gemm: unknown epilogue";
+  if ((g.role == ROLE_QKV && (g.epi != EPI_BF16 || g.N % 256)) || (g.role == ROLE_W13 && g.epi != EPI_SWIGLU) ||
+      ((g.role == ROLE_OUT || g.role == ROLE_W2) && g.epi != EPI_BF16) ||
+      (g.role == ROLE_EMBED && g.epi != EPI_F32_BIAS) || (g.role == ROLE_FINAL && g.epi != EPI_UNPATCH))
+    return "gemm: role and epilogue disagree";
   return nullptr;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  switch (g.role) {
+    case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_BF16, ROLE_QKV>(g, s);
+    case ROLE_OUT: return launch_epi<EPI_BF16, ROLE_OUT>(g, s);
+    case ROLE_W13: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_W13>(g, s);
+    case ROLE_W2: return launch_epi<EPI_BF16, ROLE_W2>(g, s);
+    case ROLE_EMBED: return launch_epi<EPI_F32_BIAS, ROLE_EMBED>(g, s);
+    case ROLE_FINAL: return launch_epi<EPI_UNPATCH, ROLE_FINAL>(g, s);
+    default: break;
+  }
   switch (g.epi) {
-    case EPI_BF16: return launch_epi<EPI_BF16>(g, s);
-    case EPI_F32_BIAS: return launch_epi<EPI_F32_BIAS>(g, s);
-    case EPI_SWIGLU: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU>(g, s);
-    default: return launch_epi<EPI_UNPATCH>(g, s);
+    case EPI_BF16: return launch_epi<EPI_BF16, ROLE_ANY>(g, s);
+    case EPI_F32_BIAS: return launch_epi<EPI_F32_BIAS, ROLE_ANY>(g, s);
+    case EPI_SWIGLU: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_ANY>(g, s);
+    default: return launch_epi<EPI_UNPATCH, ROLE_ANY>(g, s);
   }
 }
 

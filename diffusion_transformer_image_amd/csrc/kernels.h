@@ -12,6 +12,8 @@ namespace zimg {
 
 // ---------------------------------------------------------------- GEMM
 enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_SWIGLU = 2, EPI_UNPATCH = 3 };
+// which projection a launch is (selects the kernel symbol and tile shape)
+enum { ROLE_ANY = 0, ROLE_QKV = 1, ROLE_OUT = 2, ROLE_W13 = 3, ROLE_W2 = 4, ROLE_EMBED = 5, ROLE_FINAL = 6 };
 
 struct EpiArgs {
   void* C;            // output base
@@ -31,6 +33,7 @@ struct GemmArgs {
   int M, N, K;
   int epi;
   EpiArgs ep;
+  int role;
 };
 
 const char* gemm_check(const GemmArgs& g);  // null if OK

@@ -64,6 +64,28 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
  */
 int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void* stream);
 
+/*
+ * Per-kernel timing of forwards on a handle, for measurement: while
+ * enabled, every kernel (or small group of launches) of a forward is
+ * bracketed by HIP events recorded on the forward's stream, and the elapsed
+ * times are accumulated per class.  zimg_dit_profile(h, 1) creates the
+ * event pool once and resets the totals; zimg_dit_profile(h, 0) stops
+ * recording.  zimg_dit_profile_read() waits for recorded events and writes
+ * up to max_stats entries (name, launches, total milliseconds); *n_stats
+ * receives the number of classes.  Classes: gemm_qkv, gemm_out,
+ * gemm_w13_swiglu, gemm_w2, attention, qknorm_rope, pre_norm, post_norm,
+ * embed (patchify + caption norm + both embed GEMMs), final_layer,
+ * conditioning (timestep MLP + the adaLN projection).
+ */
+typedef struct zimg_kernel_stat {
+  const char* name; /* static string */
+  int64_t launches;
+  double total_ms;
+} zimg_kernel_stat;
+
+int zimg_dit_profile(zimg_dit* h, int32_t enable);
+int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
 #ifdef __cplusplus
 }
 #endif
