@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int64_t ld = 3 * (int64_t)D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int sw = lrow & 7;
+  const int swk = lrow & 15;         // K rows are 256 B: 16 rows per lane group on distinct banks
+  const int swv = (lrow >> 1) & 7;   // V^T rows are 128 B: two rows per 256-byte bank line
 
   // this lane's query (B operand column): rows past the tile end are clamped
   const int qi = wave * 32 + lrow;
@@ -85,12 +86,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, key = c >> 4, hc = c & 15;
       const int R = (key & 32) | swap_bits23(key & 31);
-      *reinterpret_cast<u32x4*>(&Ks[buf][R * HD + ((hc ^ (R & 7)) << 3)]) = rk[i];
+      *reinterpret_cast<u32x4*>(&Ks[buf][R * HD + ((hc ^ (R & 15)) << 3)]) = rk[i];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + 256 * i, d = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&Vs[buf][d * KTILE + ((kc ^ (d & 7)) << 3)]) = rv[i];
+      *reinterpret_cast<u32x4*>(&Vs[buf][d * KTILE + ((kc ^ ((d >> 1) & 7)) << 3)]) = rv[i];
     }
   };
 
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Ks[buf][(tt * 32 + lrow) * HD + (((2 * ks + lhalf) ^ sw) << 3)]);
+            *reinterpret_cast<const bf16x8*>(&Ks[buf][(tt * 32 + lrow) * HD + (((2 * ks + lhalf) ^ swk) << 3)]);
         st[tt] = mfma32(kf, qf[ks], st[tt]);
       }
     if (nv < KTILE) {
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&Vs[buf][(dt * 32 + lrow) * KTILE + (((2 * s + lhalf) ^ sw) << 3)]);
+            *reinterpret_cast<const bf16x8*>(&Vs[buf][(dt * 32 + lrow) * KTILE + (((2 * s + lhalf) ^ swv) << 3)]);
         o[dt] = mfma32(vf, pf, o[dt]);
       }
     }

@@ -6,12 +6,14 @@
 // the MFMA operand layout wants, so no transposition happens anywhere.
 //
 // Workgroup tile BM x BN, K-step 64, 512 threads = 8 waves (2 waves per
-// SIMD).  Each K-step is staged global -> registers -> LDS with a two-slot
-// LDS ring: the next step's global loads are issued before the current
-// step's MFMAs, and stored to the other slot after them, so one barrier per
-// step suffices.  LDS rows are 128 B (64 bf16); the 16-byte chunk c of row r
-// is stored at position c ^ (r & 7), so the 32 rows one MFMA operand read
-// touches hit distinct bank groups.
+// SIMD, so one wave's MFMAs cover the other's memory waits).  Operands go
+// global -> LDS directly (global_load_lds_dwordx4, no register staging) into
+// a two-stage ring: the next K-step's loads are issued at the start of the
+// current one, and one barrier per K-step publishes them.  LDS rows are
+// 128 B (64 bf16); the 16-byte chunk c of row r
+// is stored at position c ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 B
+// per cycle, and with two rows per 256-byte bank line this makes the 16
+// rows of each lane group land on 16 distinct bank groups.
 //
 // Epilogues (template): bf16 store; fp32 store with bias; SwiGLU, where W's
 // rows are interleaved in groups of 32 (32 rows of w1, then the same 32 rows
@@ -29,24 +31,31 @@ constexpr int BK = 64;
 constexpr int NT = 512;
 constexpr int GROUP_M = 8;
 
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 // ROLE only separates the symbols of the projections (qkv, out, w1|w3, w2,
 // embeds, final) so that profiles attribute time per projection.
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
-__global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
-                                                  const bf16_t* __restrict__ W, int64_t ldw,
-                                                  int M, int N, int K, EpiArgs ep, int tiles_m,
-                                                  int tiles_n) {
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
+                                                     const bf16_t* __restrict__ W, int64_t ldw,
+                                                     int M, int N, int K, EpiArgs ep, int tiles_m,
+                                                     int tiles_n) {
   static_assert(WM * WN == NT / 64, "8 waves");
+  constexpr int NW = NT / 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   static_assert(TM >= 1 && TN >= 1, "wave tile at least 32x32");
   static_assert(EPI != EPI_SWIGLU || (TN % 2) == 0, "swiglu pairs 32-col subtiles");
-  constexpr int A_CH = BM * 8 / NT;  // 16-byte chunks per thread per K-step
-  constexpr int B_CH = BN * 8 / NT;
-  static_assert(A_CH >= 1 && B_CH >= 1, "tile too small for 512 threads");
+  constexpr int NA = BM * 8 / 64 / NW;  // direct-to-LDS loads per wave per K-step (1 KB each)
+  constexpr int NB = BN * 8 / 64 / NW;
+  static_assert(NA >= 1 && NB >= 1, "tile too small for 8 waves");
 
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * BK];
+  // two stages in separate arrays, so the compiler can see that loads into
+  // one stage never alias reads of the other
+  __shared__ __attribute__((aligned(16))) bf16_t As0[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs0[BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t As1[BM * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs1[BN * BK];
 
   // tile id: XCD-contiguous, then grouped along M
   const int total = tiles_m * tiles_n;
@@ -61,38 +70,28 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
 
-  // global source pointers (rows clamped into range) and LDS destinations
-  const bf16_t* a_src[A_CH];
-  int a_dst[A_CH];
+  // A wave's load i fills 1 KB of LDS = 64 chunks of 16 B, chunk p = (i*NW + wid)*64 + lane,
+  // i.e. row p/8, stored position p%8; it fetches the logical chunk stored there
+  // (rows past M or N are clamped: their results are never stored).
+  const bf16_t* a_src[NA];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + NT * i, row = c >> 3, ch = c & 7;
-    const int gr = min(m0 + row, M - 1);
-    a_src[i] = A + (int64_t)gr * lda + ch * 8;
-    a_dst[i] = row * BK + ((ch ^ (row & 7)) << 3);
+  for (int i = 0; i < NA; ++i) {
+    const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+    a_src[i] = A + (int64_t)min(m0 + row, M - 1) * lda + lc * 8;
   }
-  const bf16_t* b_src[B_CH];
-  int b_dst[B_CH];
+  const bf16_t* b_src[NB];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + NT * i, row = c >> 3, ch = c & 7;
-    const int gr = min(n0 + row, N - 1);
-    b_src[i] = W + (int64_t)gr * ldw + ch * 8;
-    b_dst[i] = row * BK + ((ch ^ (row & 7)) << 3);
+  for (int i = 0; i < NB; ++i) {
+    const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
+    b_src[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + lc * 8;
   }
-
-  u32x4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int kt) {
+  auto issue = [&](int kt, bf16_t* as, bf16_t* bs) {
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const u32x4*>(a_src[i] + kt * BK);
+    for (int i = 0; i < NA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kt * BK), LDS_PTR(as + (i * NW + wid) * 512), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const u32x4*>(b_src[i] + kt * BK);
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<u32x4*>(&As[buf][a_dst[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<u32x4*>(&Bs[buf][b_dst[i]]) = rb[i];
+    for (int i = 0; i < NB; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kt * BK), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
   };
 
   f32x16 acc[TM][TN];
@@ -101,38 +100,59 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, 
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-  // per-lane LDS read offsets for operand rows
   const int lrow = lane & 31, lhalf = lane >> 5;
-  int a_off[TM], b_off[TN];
+  const int sw = (lrow >> 1) & 7;  // subtile bases are multiples of 32 rows
+  const int aoff = (wm * WTM + lrow) * BK, boff = (wn * WTN + lrow) * BK;
+  bf16x8 af[2][TM], bfr[2][TN];
+  auto frags = [&](const bf16_t* as, const bf16_t* bs, int kk, int set) {
+    const int ch = ((kk * 2 + lhalf) ^ sw) << 3;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) a_off[i] = (wm * WTM + i * 32 + lrow) * BK;
+    for (int i = 0; i < TM; ++i) af[set][i] = *reinterpret_cast<const bf16x8*>(as + aoff + i * 32 * BK + ch);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) b_off[j] = (wn * WTN + j * 32 + lrow) * BK;
-  const int sw = lrow & 7;  // (row & 7) is lrow & 7 because subtile bases are multiples of 32
-
-  const int KT = K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    for (int j = 0; j < TN; ++j) bfr[set][j] = *reinterpret_cast<const bf16x8*>(bs + boff + j * 32 * BK + ch);
+  };
+  // One K-step: start the next stage's loads, then four k16 steps in which the
+  // operand reads of step k+1 are interleaved one-for-one with the MFMAs of
+  // step k (the scheduling barriers pin that order), so LDS latency hides
+  // behind matrix-core work.
+  auto step = [&](const bf16_t* as, const bf16_t* bs, bool do_issue, int kt_next, bf16_t* nas, bf16_t* nbs) {
+    if (do_issue) issue(kt_next, nas, nbs);
+    frags(as, bs, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, NA + NB, 0);  // VMEM (the loads above)
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of step 0
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int ch = ((kk * 2 + lhalf) ^ sw) << 3;
-      bf16x8 af[TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const bf16x8*>(&As[buf][a_off[i] + ch]);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][b_off[j] + ch]);
+      if (kk + 1 < BK / 16) frags(as, bs, kk + 1, (kk + 1) & 1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+      if (kk + 1 < BK / 16) {
+        constexpr int PAIRS = (TM + TN) < (TM * TN) ? (TM + TN) : (TM * TN);
+#pragma unroll
+        for (int g = 0; g < PAIRS; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
+        if (TM + TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN - PAIRS, 0);
+        if (TM * TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - PAIRS, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+      }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  };
+
+  const int KT = K / BK;
+  issue(0, As0, Bs0);
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {
+    step(As0, Bs0, true, kt + 1, As1, Bs1);
+    __syncthreads();
+    step(As1, Bs1, kt + 2 < KT, kt + 2, As0, Bs0);
     __syncthreads();
   }
+  if (kt < KT) step(As0, Bs0, false, 0, As1, Bs1);
 
   // epilogue: element e = ii*4 + jj of subtile (i, j) is row
   // i*32 + ii*8 + lhalf*4 + jj, column j*32 + lrow of the wave tile.
@@ -190,6 +210,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(const bf16_t* __restrict__ A, 
 
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
+  static_assert(2 * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE>), dim3(tiles_m * tiles_n), dim3(NT), 0, s,
                      g.A, g.lda, g.W, g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n);
