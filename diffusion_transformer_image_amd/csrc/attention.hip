@@ -10,8 +10,9 @@
 //
 // Workgroup = 4 waves = 128 queries of one head; each wave owns 32 queries.
 // Keys stream through LDS in tiles of 64 (K as [key][128], V as the
-// transposed [128][key] tile read from vT), double-buffered: the next tile's
-// global loads are in flight while the current tile is computed.
+// transposed [128][key] tile read from vT) by direct global->LDS loads into
+// double buffers; scores of the next tile are computed while the current
+// tile's softmax runs, so matrix-core and vector work overlap.
 //
 // Orientation.  Scores are computed transposed, S^T = K Q^T, with the MFMA
 // A operand = 32 keys and B operand = 32 queries, so every lane holds 16
@@ -31,12 +32,18 @@ namespace {
 
 constexpr int HD = 128;  // head_dim
 constexpr int KTILE = 64;
+constexpr float RESCALE_SLACK = 8.0f;  // log2 units: stale row max may lag by 2^8
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 ZI_DEV int swap_bits23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KTILE * HD];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][HD * KTILE];
+  // K tiles [64 keys][128] and V^T tiles [128][64 keys], two of each
+  __shared__ __attribute__((aligned(16))) bf16_t K0[KTILE * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t K1[KTILE * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t V0[HD * KTILE];
+  __shared__ __attribute__((aligned(16))) bf16_t V1[HD * KTILE];
 
   const int total = a.n_items * a.H;
   const int lid = xcd_remap(blockIdx.x, total);
@@ -47,8 +54,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int64_t ld = 3 * (int64_t)D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int swk = lrow & 15;         // K rows are 256 B: 16 rows per lane group on distinct banks
-  const int swv = (lrow >> 1) & 7;   // V^T rows are 128 B: two rows per 256-byte bank line
+  const int swk = lrow & 15;        // K rows are 256 B: 16 rows per lane group on distinct banks
+  const int swv = (lrow >> 1) & 7;  // V^T rows are 128 B: two rows per 256-byte bank line
 
   // this lane's query (B operand column): rows past the tile end are clamped
   const int qi = wave * 32 + lrow;
@@ -62,37 +69,58 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   const int nt0 = (sg.n[0] + KTILE - 1) / KTILE;
   const int nt1 = (sg.n[1] + KTILE - 1) / KTILE;
-  const int ntiles = nt0 + nt1;
+  const int T = nt0 + nt1;
+  auto tile_start = [&](int t) { return t < nt0 ? sg.r0[0] + t * KTILE : sg.r0[1] + (t - nt0) * KTILE; };
+  auto tile_valid = [&](int t) {
+    return t < nt0 ? min(KTILE, sg.n[0] - t * KTILE) : min(KTILE, sg.n[1] - (t - nt0) * KTILE);
+  };
 
-  u32x4 rk[4], rv[4];
-  auto gload = [&](int t) {
-    const bool first = t < nt0;
-    const int off = (first ? t : t - nt0) * KTILE;
-    const int kr0 = (first ? sg.r0[0] : sg.r0[1]) + off;
-    const int nv = min(KTILE, (first ? sg.n[0] : sg.n[1]) - off);
+  // Direct global -> LDS loads: a wave's load i fills 1 KB = 64 chunks of 16 B.
+  // K: chunk p -> LDS row R = p/16 (holds key 32*(R/32) + swap_bits23(R%32)),
+  //    stored position p%16 holds logical chunk (p%16) ^ (R & 15).
+  // V^T: chunk p -> row d = p/8, stored position p%8 holds keys 8*((p%8) ^ ((d>>1)&7)).
+  auto dma_k = [&](int t, bf16_t* kb) {
+    const int kr0 = tile_start(t), nv = tile_valid(t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, key = c >> 4, hc = c & 15;
-      rk[i] = *reinterpret_cast<const u32x4*>(a.qkv + (int64_t)(kr0 + min(key, nv - 1)) * ld + D + h * HD + hc * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, d = c >> 3, kc = c & 7;
-      rv[i] = *reinterpret_cast<const u32x4*>(a.vT + (int64_t)(h * HD + d) * a.S_pad + kr0 + kc * 8);
+      const int p = (i * 4 + wave) * 64 + lane, R = p >> 4, hc = (p & 15) ^ (R & 15);
+      const int key = (R & 32) | swap_bits23(R & 31);
+      const bf16_t* src = a.qkv + (int64_t)(kr0 + min(key, nv - 1)) * ld + D + h * HD + hc * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
+  auto dma_v = [&](int t, bf16_t* vb) {
+    const int kr0 = tile_start(t);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, key = c >> 4, hc = c & 15;
-      const int R = (key & 32) | swap_bits23(key & 31);
-      *reinterpret_cast<u32x4*>(&Ks[buf][R * HD + ((hc ^ (R & 15)) << 3)]) = rk[i];
+      const int p = (i * 4 + wave) * 64 + lane, d = p >> 3, kc = (p & 7) ^ ((d >> 1) & 7);
+      const bf16_t* src = a.vT + (int64_t)(h * HD + d) * a.S_pad + kr0 + kc * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(vb + (i * 4 + wave) * 512), 16, 0, 0);
     }
+  };
+  // S^T for 64 keys x this wave's 32 queries; with MASK, keys past nv -> -inf
+  auto qk = [&](const bf16_t* kb, f32x16* st) {
+    st[0] = f32x16{};
+    st[1] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, d = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(&Vs[buf][d * KTILE + ((kc ^ ((d >> 1) & 7)) << 3)]) = rv[i];
-    }
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (tt * 32 + lrow) * HD + (((2 * ks + lhalf) ^ swk) << 3));
+        st[tt] = mfma32(kf, qf[ks], st[tt]);
+      }
+  };
+  auto mask = [&](f32x16* st, int nv) {
+    // key of element e is c_e + 8*lhalf with c_e a compile-time constant;
+    // comparing c_e against nv - 8*lhalf keeps the constants as immediates
+    const int nvl = nv - lhalf * 8;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = tt * 32 + 16 * (e >> 3) + ((e >> 2) & 1) * 4 + (e & 3);
+        st[tt][e] = c < nvl ? st[tt][e] : -INFINITY;
+      }
   };
 
   f32x16 o[4];
@@ -101,61 +129,37 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale_log2;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const int nv = (t < nt0) ? min(KTILE, sg.n[0] - t * KTILE) : min(KTILE, sg.n[1] - (t - nt0) * KTILE);
-
-    // S^T for 64 keys x 32 queries
-    f32x16 st[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&Ks[buf][(tt * 32 + lrow) * HD + (((2 * ks + lhalf) ^ swk) << 3)]);
-        st[tt] = mfma32(kf, qf[ks], st[tt]);
-      }
-    if (nv < KTILE) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = tt * 32 + 16 * (e >> 3) + lhalf * 8 + ((e >> 2) & 1) * 4 + (e & 3);
-          if (key >= nv) st[tt][e] = -INFINITY;
-        }
-    }
-
-    // online softmax in the log2 domain
+  // Online softmax of one score tile in the log2 domain (raw v_exp_f32:
+  // weights below 2^-126 flush to zero).  The reference max m only moves when
+  // a lane's max exceeds it by the slack, so p <= 2^slack; the O rescale is
+  // branch-free (alpha = 1 when m did not move).
+  auto softmax = [&](f32x16* st) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[tt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(m, mx * sl2);
-    const float alpha = exp2f(m - mnew);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    const float mnew = mx > m + RESCALE_SLACK ? mx : m;
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
     float rs = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(fmaf(st[tt][e], sl2, -mnew));
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], sl2, -m));
         st[tt][e] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32, 64);
-    l = fmaf(l, alpha, rs);
-    m = mnew;
+    l = fmaf(l, alpha, rs + __shfl_xor(rs, 32, 64));
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
-
-    // O^T += V^T P^T over 4 key-steps of 16
+  };
+  // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
+  auto pv = [&](const bf16_t* vb, const f32x16* st) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 pf;
@@ -163,13 +167,64 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       for (int u = 0; u < 8; ++u) pf[u] = (__bf16)st[s >> 1][(s & 1) * 8 + u];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(&Vs[buf][(dt * 32 + lrow) * KTILE + (((2 * s + lhalf) ^ swv) << 3)]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + (dt * 32 + lrow) * KTILE + (((2 * s + lhalf) ^ swv) << 3));
         o[dt] = mfma32(vf, pf, o[dt]);
       }
     }
-    if (t + 1 < ntiles) sstore(buf ^ 1);
+  };
+  // the issue order of one pipelined half: scores of the next tile interleaved
+  // with the softmax of the current one, then the PV product
+  auto pin_order = [&]() {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0); // VALU (softmax)
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (V operand)
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
+    }
+  };
+
+  // Pipeline: in the half that handles tile t, the scores of tile t+1 are
+  // computed while tile t is normalised and multiplied into O.  K(t+2) and
+  // V(t+1) are loaded meanwhile into the buffers freed by the previous half.
+  // A half contains no branches (the mask is always applied), so the
+  // scheduler can interleave matrix and vector work.
+  auto half = [&](const bf16_t* kn, const bf16_t* vc, f32x16* scur, f32x16* snext, int nv_next) {
+    qk(kn, snext);
+    mask(snext, nv_next);
+    softmax(scur);
+    pv(vc, scur);
+    pin_order();
+  };
+
+  // The tile count is padded to an even number (>= 2) with empty tiles: no
+  // loads, every score masked, so their weights are exactly zero.  The loop
+  // body is then the same for every pair of tiles, with no tail.
+  const int Tp = T + (T & 1);
+  auto nvalid = [&](int tt) { return tt < T ? tile_valid(tt) : 0; };
+  dma_k(0, K0);
+  dma_v(0, V0);
+  if (1 < T) dma_k(1, K1);
+  __syncthreads();
+  f32x16 sc[2], sn[2];
+  qk(K0, sc);
+  mask(sc, nvalid(0));
+  for (int t = 0; t < Tp; t += 2) {
+    __syncthreads();  // K(t+1), V(t) landed; everyone is done with K(t) and V(t-1)
+    if (t + 2 < T) dma_k(t + 2, K0);
+    if (t + 1 < T) dma_v(t + 1, V1);
+    const int nv1 = nvalid(t + 1);
+    half(K1, V0, sc, sn, nv1);
     __syncthreads();
+    if (t + 3 < T) dma_k(t + 3, K1);
+    if (t + 2 < T) dma_v(t + 2, V0);
+    const int nv2 = nvalid(t + 2);  // past the end: a throwaway, fully masked tile
+    half(K0, V1, sn, sc, nv2);
   }
 
   if (qi < it.nq) {

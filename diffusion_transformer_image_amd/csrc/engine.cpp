@@ -317,6 +317,9 @@ struct zimg_dit {
   std::vector<int32_t> table_key;
   int n_items_stage[3] = {0, 0, 0};
 
+  // GEMM split-K workspace (partials of the last wave's tiles)
+  zimg::GemmSplit split{};
+
   // capture
   float* cap_buf = nullptr;
   size_t cap_bytes = 0;
@@ -504,6 +507,12 @@ int zimg_dit::allocate() {
   max_items = S_max / 16 + 2 * (int64_t)c.max_batch + 8;  // q-tiles of 128 over ranges of >= 16 rows
   ALLOC(segs, 3 * (int64_t)c.max_batch);
   ALLOC(items, 3 * max_items);
+  int n_cu = 0;
+  HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device));
+  split.n_cu = n_cu;
+  split.max_tiles = 2 * n_cu;
+  split.ws_bytes = (size_t)2 * n_cu * 256 * 256 * 4;  // one partial tile per resident workgroup
+  ALLOC(split.ws, split.ws_bytes / 4);
 #undef ALLOC
   staging_bytes = (size_t)S_max * 64 * 4 * 2 + (size_t)S_max * 4 + 3 * c.max_batch * sizeof(zimg::AttnSeg) +
                   3 * max_items * sizeof(zimg::AttnItem);
@@ -691,6 +700,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = qkv + (int64_t)r0 * 3 * D;
   ga.ep.ldc = 3 * D;
   ga.role = zimg::ROLE_QKV;
+  ga.split = split;
   PROFILED(K_QKV, zimg::launch_gemm(ga, s));
 
   zimg::QKRopeArgs qa{qkv, vT, w.nq, w.nk, cos_t, sin_t, r0, r1, H, (int)S_pad, c.norm_eps};
@@ -706,6 +716,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
   ga.role = zimg::ROLE_OUT;
+  ga.split = split;
   PROFILED(K_OUT, zimg::launch_gemm(ga, s));
 
   zimg::PostNormArgs pn{};
@@ -734,6 +745,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = g + (int64_t)r0 * F;
   ga.ep.ldc = F;
   ga.role = zimg::ROLE_W13;
+  ga.split = split;
   PROFILED(K_W13, zimg::launch_gemm(ga, s));
 
   ga.A = g + (int64_t)r0 * F;
@@ -746,6 +758,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
   ga.role = zimg::ROLE_W2;
+  ga.split = split;
   PROFILED(K_W2, zimg::launch_gemm(ga, s));
 
   pn.w_post = w.fn2;
@@ -791,6 +804,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.K = P;
   ga.epi = zimg::EPI_F32_BIAS;
   ga.role = zimg::ROLE_EMBED;
+  ga.split = split;
   ga.ep.C = x;
   ga.ep.ldc = D;
   ga.ep.bias = x_b;
@@ -850,6 +864,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.K = D;
   ga.epi = zimg::EPI_UNPATCH;
   ga.role = zimg::ROLE_FINAL;
+  ga.split = split;
   ga.ep.C = out;
   ga.ep.bias = fin_b;
   ga.ep.ntok = L.N;

@@ -33,13 +33,74 @@ constexpr int GROUP_M = 8;
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Epilogue: element e = ii*4 + jj of subtile (i, j) of a wave is row
+// i*32 + ii*8 + lhalf*4 + jj, column j*32 + lrow of the wave tile.
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0, int M, int N,
+                                         const EpiArgs& ep) {
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int rbase = m0 + wm * WTM;
+  const int cbase = n0 + wn * WTN;
+  if constexpr (EPI == EPI_SWIGLU) {
+    bf16_t* C = reinterpret_cast<bf16_t*>(ep.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; j += 2) {
+        const int col = ((cbase + j * 32) >> 1) + lrow;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+          if (row < M) {
+            const float a1 = acc[i][j][e], a3 = acc[i][j + 1][e];
+            const float s = a1 / (1.0f + __expf(-a1));
+            C[(int64_t)row * ep.ldc + col] = f2bf(s * a3);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = cbase + j * 32 + lrow;
+        if (col >= N) continue;
+        float bias = 0.f;
+        if constexpr (EPI != EPI_BF16) bias = ep.bias ? ep.bias[col] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = rbase + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+          if (row >= M) continue;
+          const float v = acc[i][j][e];
+          if constexpr (EPI == EPI_BF16) {
+            reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + col] = f2bf(v);
+          } else if constexpr (EPI == EPI_F32_BIAS) {
+            reinterpret_cast<float*>(ep.C)[(int64_t)row * ep.ldc + col] = v + bias;
+          } else {  // EPI_UNPATCH: row = token of the batch, col = (a*p + b)*C + ch
+            const int b = row / ep.npad, n = row - b * ep.npad;
+            if (n >= ep.ntok) continue;  // alignment padding row
+            const int pi = n / ep.Wp, pj = n - pi * ep.Wp;
+            const int ab = col / ep.C_ch, ch = col - ab * ep.C_ch;
+            const int pa = ab / ep.patch, pb = ab - pa * ep.patch;
+            const int Hl = ep.Hp * ep.patch, Wl = ep.Wp * ep.patch;
+            reinterpret_cast<float*>(ep.C)[(((int64_t)b * ep.C_ch + ch) * Hl + pi * ep.patch + pa) * Wl +
+                                           pj * ep.patch + pb] = v + bias;
+          }
+        }
+      }
+  }
+}
+
 // ROLE only separates the symbols of the projections (qkv, out, w1|w3, w2,
 // embeds, final) so that profiles attribute time per projection.
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                      const bf16_t* __restrict__ W, int64_t ldw,
                                                      int M, int N, int K, EpiArgs ep, int tiles_m,
-                                                     int tiles_n) {
+                                                     int tiles_n, int full_tiles, int nsplit, float* ws) {
   static_assert(WM * WN == NT / 64, "8 waves");
   constexpr int NW = NT / 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -57,9 +118,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) bf16_t As1[BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t Bs1[BN * BK];
 
-  // tile id: XCD-contiguous, then grouped along M
+  // Work unit -> tile.  The first full_tiles units are whole tiles; each of
+  // the remaining (total - full_tiles) tiles is split into nsplit K-ranges.
   const int total = tiles_m * tiles_n;
-  const int lid = xcd_remap(blockIdx.x, total);
+  // full tiles and split units are spread over the XCDs separately (the
+  // full-tile count is a multiple of the CU count, hence of 8)
+  const int units = full_tiles + (total - full_tiles) * nsplit;
+  const int bid = blockIdx.x;
+  const int uid = bid < full_tiles ? xcd_remap(bid, full_tiles)
+                                   : full_tiles + xcd_remap(bid - full_tiles, units - full_tiles);
+  const bool is_split = uid >= full_tiles;
+  const int tail_idx = is_split ? (uid - full_tiles) / nsplit : 0;
+  const int chunk = is_split ? (uid - full_tiles) - tail_idx * nsplit : 0;
+  const int lid = is_split ? full_tiles + tail_idx : uid;  // tile id in grouped order
   const int per_group = GROUP_M * tiles_n;
   const int first_m = (lid / per_group) * GROUP_M;
   const int gsize = min(tiles_m - first_m, GROUP_M);
@@ -142,10 +213,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
     }
   };
 
-  const int KT = K / BK;
-  issue(0, As0, Bs0);
+  const int KTALL = K / BK;
+  const int kt0 = is_split ? (int)((int64_t)chunk * KTALL / nsplit) : 0;
+  const int KT = is_split ? (int)((int64_t)(chunk + 1) * KTALL / nsplit) : KTALL;
+  issue(kt0, As0, Bs0);
   __syncthreads();
-  int kt = 0;
+  int kt = kt0;
   for (; kt + 2 <= KT; kt += 2) {
     step(As0, Bs0, true, kt + 1, As1, Bs1);
     __syncthreads();
@@ -154,66 +227,129 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   }
   if (kt < KT) step(As0, Bs0, false, 0, As1, Bs1);
 
-  // epilogue: element e = ii*4 + jj of subtile (i, j) is row
-  // i*32 + ii*8 + lhalf*4 + jj, column j*32 + lrow of the wave tile.
-  const int rbase = m0 + wm * WTM;
-  const int cbase = n0 + wn * WTN;
-  if constexpr (EPI == EPI_SWIGLU) {
-    bf16_t* C = reinterpret_cast<bf16_t*>(ep.C);
+  if (is_split) {
+    // A split unit stores its fp32 partial (accumulator order, lanes
+    // contiguous) and stops; gemm_reduce_kernel sums the partials of each
+    // split tile in chunk order and runs the epilogue.
+    float* part = ws + ((int64_t)tail_idx * nsplit + chunk) * (BM * BN);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; j += 2) {
-        const int col = ((cbase + j * 32) >> 1) + lrow;
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          if (row < M) {
-            const float a1 = acc[i][j][e], a3 = acc[i][j + 1][e];
-            const float s = a1 / (1.0f + __expf(-a1));
-            C[(int64_t)row * ep.ldc + col] = f2bf(s * a3);
-          }
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = cbase + j * 32 + lrow;
-        if (col >= N) continue;
-        float bias = 0.f;
-        if constexpr (EPI != EPI_BF16) bias = ep.bias ? ep.bias[col] : 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = rbase + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          if (row >= M) continue;
-          const float v = acc[i][j][e];
-          if constexpr (EPI == EPI_BF16) {
-            reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + col] = f2bf(v);
-          } else if constexpr (EPI == EPI_F32_BIAS) {
-            reinterpret_cast<float*>(ep.C)[(int64_t)row * ep.ldc + col] = v + bias;
-          } else {  // EPI_UNPATCH: row = token of the batch, col = (a*p + b)*C + ch
-            const int b = row / ep.npad, n = row - b * ep.npad;
-            if (n >= ep.ntok) continue;  // alignment padding row
-            const int pi = n / ep.Wp, pj = n - pi * ep.Wp;
-            const int ab = col / ep.C_ch, ch = col - ab * ep.C_ch;
-            const int pa = ab / ep.patch, pb = ab - pa * ep.patch;
-            const int Hl = ep.Hp * ep.patch, Wl = ep.Wp * ep.patch;
-            reinterpret_cast<float*>(ep.C)[(((int64_t)b * ep.C_ch + ch) * Hl + pi * ep.patch + pa) * Wl +
-                                           pj * ep.patch + pb] = v + bias;
-          }
-        }
-      }
+        for (int e = 0; e < 16; ++e) part[((i * TN + j) * 16 + e) * NT + tid] = acc[i][j][e];
+    return;
   }
+  epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
+}
+
+// Sum of the nsplit partials of each split tile, in chunk order (so the
+// result does not depend on which unit finished first), then the epilogue,
+// element by element.  A partial holds the accumulators of the producing
+// workgroup in order q = ((i*TN + j)*16 + e)*NT + tid; each thread of this
+// kernel owns a few q and recovers (row, column) from them.  SwiGLU takes
+// the w1/w3 pair (j, j+1) together.
+constexpr int RED_PER_THREAD = 4;
+
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs ep, int tiles_m, int tiles_n,
+                                                          int full_tiles, int nsplit, const float* __restrict__ ws) {
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  constexpr int TILE_F = BM * BN;
+  constexpr int SLOTS = (EPI == EPI_SWIGLU) ? TILE_F / 2 : TILE_F;  // outputs per tile
+  constexpr int PER_WG = 256 * RED_PER_THREAD;
+  constexpr int WG_PER_TILE = SLOTS / PER_WG;
+  const int tail_idx = blockIdx.x / WG_PER_TILE;
+  const int lid = full_tiles + tail_idx;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (lid / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int m0 = (first_m + (lid % per_group) % gsize) * BM;
+  const int n0 = ((lid % per_group) / gsize) * BN;
+  const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F;
+#pragma unroll
+  for (int r = 0; r < RED_PER_THREAD; ++r) {
+    const int slot = (blockIdx.x % WG_PER_TILE) * PER_WG + r * 256 + threadIdx.x;
+    // slot -> accumulator index q (SwiGLU: the w1 half, j even)
+    int q = slot;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int tid_ = slot % NT, rest = slot / NT;  // rest = (i*(TN/2) + jp)*16 + e
+      const int e = rest % 16, ijp = rest / 16, jp = ijp % (TN / 2), i = ijp / (TN / 2);
+      q = ((i * TN + 2 * jp) * 16 + e) * NT + tid_;
+    }
+    const int tid_ = q % NT, e = (q / NT) % 16, ij = q / NT / 16, j = ij % TN, i = ij / TN;
+    const int wid = tid_ >> 6, lane = tid_ & 63, wm = wid / WN, wn = wid % WN;
+    const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
+    float v = 0.f, v3 = 0.f;
+    for (int c = 0; c < nsplit; ++c) {
+      v += part[(int64_t)c * TILE_F + q];
+      if constexpr (EPI == EPI_SWIGLU) v3 += part[(int64_t)c * TILE_F + q + 16 * NT];
+    }
+    if (row >= M || col >= N) continue;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const float s = v / (1.0f + __expf(-v));
+      const int ocol = ((n0 + wn * WTN + j * 32) >> 1) + (lane & 31);
+      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + ocol] = f2bf(s * v3);
+    } else if constexpr (EPI == EPI_BF16) {
+      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + col] = f2bf(v);
+    } else if constexpr (EPI == EPI_F32_BIAS) {
+      reinterpret_cast<float*>(ep.C)[(int64_t)row * ep.ldc + col] = v + (ep.bias ? ep.bias[col] : 0.f);
+    } else {
+      const int b = row / ep.npad, n = row - b * ep.npad;
+      if (n >= ep.ntok) continue;
+      const int pi = n / ep.Wp, pj = n - pi * ep.Wp;
+      const int ab = col / ep.C_ch, ch = col - ab * ep.C_ch;
+      const int pa = ab / ep.patch, pb = ab - pa * ep.patch;
+      const int Hl = ep.Hp * ep.patch, Wl = ep.Wp * ep.patch;
+      reinterpret_cast<float*>(ep.C)[(((int64_t)b * ep.C_ch + ch) * Hl + pi * ep.patch + pa) * Wl + pj * ep.patch +
+                                     pb] = v + (ep.bias ? ep.bias[col] : 0.f);
+    }
+  }
+}
+
+// How to split the last wave: with P workgroups running at once, T tiles
+// take T / P full waves plus a partial one of r = T % P tiles.  Splitting
+// each of the r tiles into s K-ranges turns the partial wave into
+// ceil(r s / P) waves of 1/s the length; pick the s (at least two K-steps per
+// range, partial sums must fit the workspace) with the shortest time.
+int choose_split(int T, int KT, int tile_bytes, const GemmSplit& sp) {
+  if (!sp.ws || sp.n_cu <= 0) return 1;
+  const int r = T % sp.n_cu;
+  if (r == 0 || 2 * r > sp.n_cu) return 1;  // a more than half-full last wave is left alone
+  int best = 1;
+  double best_cost = 1.0;
+  for (int s = 2; s <= 32 && KT / s >= 4; ++s) {  // at least 4 K-steps per range
+    if (r > sp.max_tiles || (size_t)r * s * tile_bytes > sp.ws_bytes) break;
+    // waves of the split part (in tile times) + the reduction's reads of s partials
+    const double cost = (double)((r * s + sp.n_cu - 1) / sp.n_cu) / s + 0.01 * s;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   static_assert(2 * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE>), dim3(tiles_m * tiles_n), dim3(NT), 0, s,
-                     g.A, g.lda, g.W, g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n);
+  const int T = tiles_m * tiles_n;
+  constexpr int LDS_BYTES = 2 * (BM + BN) * BK * 2;
+  GemmSplit sp = g.split;
+  sp.n_cu *= (160 * 1024) / LDS_BYTES;  // workgroups resident at once
+  const int nsplit = choose_split(T, g.K / BK, BM * BN * 4, sp);
+  const int full = nsplit > 1 ? T - T % sp.n_cu : T;
+  const int units = full + (T - full) * nsplit;
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE>), dim3(units), dim3(NT), 0, s, g.A, g.lda, g.W,
+                     g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  constexpr int SLOTS = (EPI == EPI_SWIGLU) ? BM * BN / 2 : BM * BN;
+  static_assert(SLOTS % (256 * RED_PER_THREAD) == 0, "reduce grid");
+  hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WM, WN, EPI>), dim3((T - full) * (SLOTS / (256 * RED_PER_THREAD))),
+                     dim3(256), 0, s, g.M, g.N, g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
   return hipGetLastError();
 }
 

@@ -25,6 +25,16 @@ struct EpiArgs {
   int ntok, npad, Hp, Wp, C_ch, patch;
 };
 
+// Split of the last, partial wave of tiles along K (see gemm.hip): null
+// ``ws`` disables it.  ``ws`` holds the fp32 partial tiles (scratch; no
+// state survives a launch).
+struct GemmSplit {
+  float* ws;
+  size_t ws_bytes;
+  int max_tiles;  // split tiles the workspace may hold
+  int n_cu;       // compute units
+};
+
 struct GemmArgs {
   const bf16_t* A;
   int64_t lda;
@@ -34,6 +44,7 @@ struct GemmArgs {
   int epi;
   EpiArgs ep;
   int role;
+  GemmSplit split;
 };
 
 const char* gemm_check(const GemmArgs& g);  // null if OK
