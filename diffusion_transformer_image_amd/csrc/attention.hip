@@ -210,17 +210,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   dma_k(0, K0);
   dma_v(0, V0);
   if (1 < T) dma_k(1, K1);
-  __syncthreads();
+  dma_barrier();
   f32x16 sc[2], sn[2];
   qk(K0, sc);
   mask(sc, nvalid(0));
   for (int t = 0; t < Tp; t += 2) {
-    __syncthreads();  // K(t+1), V(t) landed; everyone is done with K(t) and V(t-1)
+    dma_barrier();  // K(t+1), V(t) landed; everyone is done with K(t) and V(t-1)
     if (t + 2 < T) dma_k(t + 2, K0);
     if (t + 1 < T) dma_v(t + 1, V1);
     const int nv1 = nvalid(t + 1);
     half(K1, V0, sc, sn, nv1);
-    __syncthreads();
+    dma_barrier();
     if (t + 3 < T) dma_k(t + 3, K1);
     if (t + 2 < T) dma_v(t + 2, V0);
     const int nv2 = nvalid(t + 2);  // past the end: a throwaway, fully masked tile

@@ -35,6 +35,15 @@ ZI_DEV f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Barrier that publishes direct global->LDS loads: each wave first waits for
+// its own outstanding loads (vmcnt), then all waves meet.  Written out
+// explicitly because the compiler does not always place that wait before a
+// loop-header barrier, and a wave's wait covers only its own loads.
+ZI_DEV void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 ZI_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

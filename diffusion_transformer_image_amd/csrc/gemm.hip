@@ -217,13 +217,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   const int kt0 = is_split ? (int)((int64_t)chunk * KTALL / nsplit) : 0;
   const int KT = is_split ? (int)((int64_t)(chunk + 1) * KTALL / nsplit) : KTALL;
   issue(kt0, As0, Bs0);
-  __syncthreads();
+  dma_barrier();
   int kt = kt0;
   for (; kt + 2 <= KT; kt += 2) {
     step(As0, Bs0, true, kt + 1, As1, Bs1);
-    __syncthreads();
+    dma_barrier();
     step(As1, Bs1, kt + 2 < KT, kt + 2, As0, Bs0);
-    __syncthreads();
+    dma_barrier();
   }
   if (kt < KT) step(As0, Bs0, false, 0, As1, Bs1);
 

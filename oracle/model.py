@@ -233,7 +233,7 @@ def swiglu_ffn(W, prefix, h):
     return (silu(a) * b) @ _f64(W[f"{prefix}.feed_forward.w2.weight"]).T
 
 
-def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None):
+def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=None):
     """One S3-DiT transformer block over a single sample's sequence x [S, D].
 
     Sandwich-norm block ([AIT] "Architecture"; [MNN] "Conversion details":
@@ -248,7 +248,8 @@ def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None):
     ``mod`` is the tuple from ``block_modulation``; None means unmodulated
     (context refiner, [AIT] "Architecture"): scales 1 and gates 1.
     ``rows`` restricts the output (and the queries) to those rows; keys and
-    values still come from every row.
+    values still come from every row.  ``taps`` (a dict), if given, receives
+    the w2 output under "ffn_out" (observation only).
     """
     D, H, hd, eps = cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.norm_eps
     x = _f64(x)
@@ -272,6 +273,8 @@ def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None):
 
     h2 = rms_norm(x1, W[f"{prefix}.ffn_norm1.weight"], eps) * scale_f
     f = swiglu_ffn(W, prefix, h2)
+    if taps is not None:
+        taps["ffn_out"] = f
     return x1 + gate_f * rms_norm(f, W[f"{prefix}.ffn_norm2.weight"], eps)
 
 
@@ -305,14 +308,15 @@ def final_layer(cfg: ModelConfig, W, x_img, c):
     return z @ _f64(W["final_layer.linear.weight"]).T + _f64(W["final_layer.linear.bias"])
 
 
-def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None):
+def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak=None):
     """Forward of one sample: latent [C, Hl, Wl], caption features [L, 2560],
     scalar model time t -> raw model output [C, Hl, Wl].
 
     Order ([AIT] "Architecture"): noise refiner over the image tokens,
     context refiner (unmodulated) over the caption tokens, then the joint
     blocks over [image; caption], then the final layer on the image tokens.
-    ``capture`` (a dict) receives the residual after each stage.
+    ``capture`` (a dict) receives the residual after each stage; ``ffn_peak``
+    (a list) receives max |w2 output| of each block (observation only).
     """
     C, Hl, Wl = np.shape(latent)
     Hp, Wp = Hl // cfg.patch, Wl // cfg.patch
@@ -334,17 +338,20 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None):
     x = None
     for prefix, modulated in block_prefixes(cfg):
         mod = block_modulation(W, prefix, c) if modulated else None
+        taps = {} if ffn_peak is not None else None
         if prefix.startswith("noise_refiner"):
-            x_img = block(cfg, W, prefix, x_img, cos_img, sin_img, mod)
+            x_img = block(cfg, W, prefix, x_img, cos_img, sin_img, mod, taps=taps)
             out = x_img
         elif prefix.startswith("context_refiner"):
-            y = block(cfg, W, prefix, y, cos_cap, sin_cap, None)
+            y = block(cfg, W, prefix, y, cos_cap, sin_cap, None, taps=taps)
             out = y
         else:
             if x is None:
                 x = np.concatenate([x_img, y])
-            x = block(cfg, W, prefix, x, cos_all, sin_all, mod)
+            x = block(cfg, W, prefix, x, cos_all, sin_all, mod, taps=taps)
             out = x
+        if ffn_peak is not None:
+            ffn_peak.append(float(np.max(np.abs(taps["ffn_out"]))))
         if capture is not None:
             capture[prefix] = out.copy()
     if x is None:
@@ -356,7 +363,7 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None):
     return unpatchify(o, C, Hl, Wl, cfg.patch)
 
 
-def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None):
+def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None, ffn_peak=None):
     """Batched forward: latent [B, C, Hl, Wl], caption_feats a list of B
     arrays [L_b, 2560] (exact lengths, no padding: [AIT] "Architecture",
     "padding dropped"), t [B] -> [B, C, Hl, Wl].  Samples are independent.
@@ -367,5 +374,5 @@ def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None):
     outs = []
     for b in range(latent.shape[0]):
         cap = captures[b] if captures is not None else None
-        outs.append(forward_sample(cfg, W, latent[b], caption_feats[b], t[b], cap))
+        outs.append(forward_sample(cfg, W, latent[b], caption_feats[b], t[b], cap, ffn_peak))
     return np.stack(outs)
