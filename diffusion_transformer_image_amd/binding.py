@@ -47,6 +47,7 @@ class Config(ctypes.Structure):
         ("t_scale", ctypes.c_float), ("max_period", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("final_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_image_tokens", ctypes.c_int32), ("max_caption_tokens", ctypes.c_int32),
+        ("batch_invariant", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -94,6 +95,7 @@ SIGNATURES = {
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
     "zimg_dit_profile": (_I32, [_P, _I32]),
     "zimg_dit_profile_read": (_I32, [_P, ctypes.POINTER(KernelStat), _I32, _I32P]),
+    "zimg_dit_attention_plan": (_I32, [_P, _I32, _I32P]),
 }
 
 _lib = None
@@ -250,6 +252,13 @@ class DiT:
         n = ctypes.c_int32()
         _check(lib().zimg_dit_profile_read(self._h, stats, 32, ctypes.byref(n)), self._h)
         return {stats[i].name.decode(): (stats[i].launches, stats[i].total_ms) for i in range(min(n.value, 32))}
+
+    def attention_plan(self, stage):
+        """(pairs, pairs computed whole, chunks per split pair) of a stage at
+        the geometry of the last forward / run_blocks call."""
+        out = (ctypes.c_int32 * 3)()
+        _check(lib().zimg_dit_attention_plan(self._h, stage, out), self._h)
+        return tuple(out)
 
     def set_capture(self, buf):
         """buf: torch CUDA fp32 tensor or None."""

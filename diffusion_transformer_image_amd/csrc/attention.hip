@@ -33,6 +33,7 @@ namespace {
 constexpr int HD = 128;  // head_dim
 constexpr int KTILE = 64;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units: stale row max may lag by 2^8
+constexpr int MAX_SPLIT = 16;          // key-tile chunks per split (item, head) pair
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -45,8 +46,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16_t V0[HD * KTILE];
   __shared__ __attribute__((aligned(16))) bf16_t V1[HD * KTILE];
 
-  const int total = a.n_items * a.H;
-  const int lid = xcd_remap(blockIdx.x, total);
+  // work unit -> (item, head) pair and key-tile chunk; split units are
+  // numbered chunk-major so that neighbours share the same K/V range
+  const int n_rest = a.n_items * a.H - a.n_full;
+  int lid, chunk = 0, unit = -1;
+  if ((int)blockIdx.x < a.n_full) {
+    lid = xcd_remap(blockIdx.x, a.n_full);
+  } else {
+    unit = xcd_remap(blockIdx.x - a.n_full, n_rest * a.split);
+    chunk = unit / n_rest;
+    lid = a.n_full + (unit - chunk * n_rest);
+  }
   const int h = lid / a.n_items;
   const AttnItem it = a.items[lid - h * a.n_items];
   const AttnSeg sg = a.segs[it.seg];
@@ -70,6 +80,12 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const int nt0 = (sg.n[0] + KTILE - 1) / KTILE;
   const int nt1 = (sg.n[1] + KTILE - 1) / KTILE;
   const int T = nt0 + nt1;
+  // this unit's key tiles [tb, tb + tn)
+  int tb = 0, tn = T;
+  if (unit >= 0) {
+    tb = T * chunk / a.split;
+    tn = T * (chunk + 1) / a.split - tb;
+  }
   auto tile_start = [&](int t) { return t < nt0 ? sg.r0[0] + t * KTILE : sg.r0[1] + (t - nt0) * KTILE; };
   auto tile_valid = [&](int t) {
     return t < nt0 ? min(KTILE, sg.n[0] - t * KTILE) : min(KTILE, sg.n[1] - (t - nt0) * KTILE);
@@ -204,30 +220,45 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
   // The tile count is padded to an even number (>= 2) with empty tiles: no
   // loads, every score masked, so their weights are exactly zero.  The loop
-  // body is then the same for every pair of tiles, with no tail.
-  const int Tp = T + (T & 1);
-  auto nvalid = [&](int tt) { return tt < T ? tile_valid(tt) : 0; };
-  dma_k(0, K0);
-  dma_v(0, V0);
-  if (1 < T) dma_k(1, K1);
+  // body is then the same for every pair of tiles, with no tail.  Indexes j
+  // are relative to the unit's first tile tb.
+  const int Tp = tn + (tn & 1);
+  auto nvalid = [&](int j) { return j < tn ? tile_valid(tb + j) : 0; };
+  dma_k(tb, K0);
+  dma_v(tb, V0);
+  if (1 < tn) dma_k(tb + 1, K1);
   dma_barrier();
   f32x16 sc[2], sn[2];
   qk(K0, sc);
   mask(sc, nvalid(0));
-  for (int t = 0; t < Tp; t += 2) {
-    dma_barrier();  // K(t+1), V(t) landed; everyone is done with K(t) and V(t-1)
-    if (t + 2 < T) dma_k(t + 2, K0);
-    if (t + 1 < T) dma_v(t + 1, V1);
-    const int nv1 = nvalid(t + 1);
+  for (int j = 0; j < Tp; j += 2) {
+    dma_barrier();  // K(j+1), V(j) landed; everyone is done with K(j) and V(j-1)
+    if (j + 2 < tn) dma_k(tb + j + 2, K0);
+    if (j + 1 < tn) dma_v(tb + j + 1, V1);
+    const int nv1 = nvalid(j + 1);
     half(K1, V0, sc, sn, nv1);
     dma_barrier();
-    if (t + 3 < T) dma_k(t + 3, K1);
-    if (t + 2 < T) dma_v(t + 2, V0);
-    const int nv2 = nvalid(t + 2);  // past the end: a throwaway, fully masked tile
+    if (j + 3 < tn) dma_k(tb + j + 3, K1);
+    if (j + 2 < tn) dma_v(tb + j + 2, V0);
+    const int nv2 = nvalid(j + 2);  // past the end: a throwaway, fully masked tile
     half(K0, V1, sn, sc, nv2);
   }
 
-  if (qi < it.nq) {
+  if (qi < it.nq && unit >= 0) {
+    // partial state of this chunk: O unnormalised (relative to 2^m), m, l
+    float* po = a.part + (int64_t)unit * (128 * HD) + qi * HD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = dt * 32 + i * 8 + lhalf * 4;
+        *reinterpret_cast<f32x4*>(po + d0) = f32x4{o[dt][i * 4 + 0], o[dt][i * 4 + 1], o[dt][i * 4 + 2], o[dt][i * 4 + 3]};
+      }
+    if (lhalf == 0) {
+      float* ml = a.part + (int64_t)n_rest * a.split * (128 * HD) + ((int64_t)unit * 128 + qi) * 2;
+      *reinterpret_cast<float2*>(ml) = make_float2(m, l);
+    }
+  } else if (qi < it.nq) {
     const float inv = 1.0f / l;
     bf16_t* op = a.out + (int64_t)(it.q0 + qi) * D + h * HD;
 #pragma unroll
@@ -242,11 +273,55 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   }
 }
 
+// Merge the chunks of one split (item, head) pair: with M the largest chunk
+// reference max, weight w_c = 2^(m_c - M); O = sum_c w_c O_c / sum_c w_c l_c,
+// summed in chunk order.
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
+  __shared__ float wt[MAX_SPLIT][128];
+  const int n_rest = a.n_items * a.H - a.n_full;
+  const int p = blockIdx.x;
+  const int lid = a.n_full + p;
+  const int h = lid / a.n_items;
+  const AttnItem it = a.items[lid - h * a.n_items];
+  const float* ml = a.part + (int64_t)n_rest * a.split * (128 * HD);
+  const int tid = threadIdx.x;
+  if (tid < it.nq) {
+    float M = -INFINITY;
+    for (int c = 0; c < a.split; ++c) M = fmaxf(M, ml[((int64_t)(c * n_rest + p) * 128 + tid) * 2]);
+    float L = 0.f;
+    for (int c = 0; c < a.split; ++c) {
+      const float* v = ml + ((int64_t)(c * n_rest + p) * 128 + tid) * 2;
+      const float w = exp2f(v[0] - M);
+      wt[c][tid] = w;
+      L += w * v[1];
+    }
+    const float inv = 1.0f / L;
+    for (int c = 0; c < a.split; ++c) wt[c][tid] *= inv;
+  }
+  __syncthreads();
+  const int D = a.H * HD;
+  for (int e = tid; e < it.nq * 32; e += 256) {
+    const int q = e >> 5, d = (e & 31) * 4;
+    f32x4 acc = {};
+    for (int c = 0; c < a.split; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + (int64_t)(c * n_rest + p) * (128 * HD) + q * HD + d);
+      acc += wt[c][q] * v;
+    }
+    u32x2 u = {pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(a.out + (int64_t)(it.q0 + q) * D + h * HD + d) = u;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (a.n_items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attention_kernel, dim3(a.n_items * a.H), dim3(256), 0, s, a);
+  const int total = a.n_items * a.H;
+  if (total <= 0) return hipSuccess;
+  const int n_rest = total - a.n_full;
+  if (a.n_full < 0 || n_rest < 0 || (n_rest > 0 && (a.split < 2 || a.split > MAX_SPLIT || !a.part)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attention_kernel, dim3(a.n_full + n_rest * (n_rest > 0 ? a.split : 0)), dim3(256), 0, s, a);
+  if (n_rest > 0) hipLaunchKernelGGL(attention_combine_kernel, dim3(n_rest), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -194,6 +194,7 @@ int check_config(const zimg_dit_config* c) {
     return set_err(ZIMG_EINVAL, "max_image_tokens must be 1..1048576");
   if (c->max_caption_tokens < 1 || c->max_caption_tokens > 512)
     return set_err(ZIMG_EUNSUPPORTED, "max_caption_tokens must be 1..512 (the caption limit of the model)");
+  if (c->batch_invariant != 0 && c->batch_invariant != 1) return set_err(ZIMG_EINVAL, "batch_invariant must be 0 or 1");
   return ZIMG_OK;
 }
 
@@ -316,9 +317,14 @@ struct zimg_dit {
   hipEvent_t staging_done = nullptr;
   std::vector<int32_t> table_key;
   int n_items_stage[3] = {0, 0, 0};
+  int attn_full[3] = {0, 0, 0};   // (item, head) pairs of a stage computed whole
+  int attn_split[3] = {1, 1, 1};  // key-range chunks of each remaining pair
 
-  // GEMM split-K workspace (partials of the last wave's tiles)
+  // GEMM split-K workspace (partials of the last wave's tiles); also holds
+  // the partial states of split attention work
   zimg::GemmSplit split{};
+  // what the GEMMs may use: nothing when results must not depend on the batch
+  zimg::GemmSplit gemm_split() const { return cfg.batch_invariant ? zimg::GemmSplit{} : split; }
 
   // capture
   float* cap_buf = nullptr;
@@ -636,6 +642,25 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
           }
       }
       n_items_stage[stg] = ni;
+      // Two attention workgroups are resident per CU.  When the pairs of the
+      // last, partial round would fill at most half of those slots, each of
+      // them is split into chunks of its key tiles (at least two tiles per
+      // chunk) so that the round is filled, with one merge launch after.
+      const int P = 2 * split.n_cu, total = ni * c.n_heads, r = total % P;
+      attn_full[stg] = total;
+      attn_split[stg] = 1;
+      if (!c.batch_invariant && r > 0 && 2 * r <= P) {
+        int tmin = 1 << 30;
+        for (int lid = total - r; lid < total; ++lid) {
+          const zimg::AttnSeg& q = sg[stg * c.max_batch + itm[stg * max_items + lid % ni].seg];
+          tmin = std::min(tmin, (q.n[0] + 63) / 64 + (q.n[1] + 63) / 64);
+        }
+        const int sp = std::min(std::min(P / r, tmin / 2), 16);
+        if (sp >= 2 && (size_t)r * sp * zimg::ATTN_PART_FLOATS * 4 <= split.ws_bytes) {
+          attn_full[stg] = total - r;
+          attn_split[stg] = sp;
+        }
+      }
     }
     HIP_TRY(hipMemcpyAsync(cos_t, cs, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
     HIP_TRY(hipMemcpyAsync(sin_t, sn, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
@@ -700,14 +725,24 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = qkv + (int64_t)r0 * 3 * D;
   ga.ep.ldc = 3 * D;
   ga.role = zimg::ROLE_QKV;
-  ga.split = split;
+  ga.split = gemm_split();
   PROFILED(K_QKV, zimg::launch_gemm(ga, s));
 
   zimg::QKRopeArgs qa{qkv, vT, w.nq, w.nk, cos_t, sin_t, r0, r1, H, (int)S_pad, c.norm_eps};
   PROFILED(K_QKROPE, zimg::launch_qknorm_rope(qa, s));
 
-  zimg::AttnArgs aa{qkv, vT, o, items + stage * max_items, segs + stage * c.max_batch, n_items_stage[stage], H,
-                    (int)S_pad, (float)(1.4426950408889634 / std::sqrt(128.0))};
+  zimg::AttnArgs aa{qkv,
+                    vT,
+                    o,
+                    items + stage * max_items,
+                    segs + stage * c.max_batch,
+                    n_items_stage[stage],
+                    H,
+                    (int)S_pad,
+                    (float)(1.4426950408889634 / std::sqrt(128.0)),
+                    attn_full[stage],
+                    attn_split[stage],
+                    split.ws};
   PROFILED(K_ATTN, zimg::launch_attention(aa, s));
 
   ga.A = o + (int64_t)r0 * D;
@@ -716,7 +751,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
   ga.role = zimg::ROLE_OUT;
-  ga.split = split;
+  ga.split = gemm_split();
   PROFILED(K_OUT, zimg::launch_gemm(ga, s));
 
   zimg::PostNormArgs pn{};
@@ -745,7 +780,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = g + (int64_t)r0 * F;
   ga.ep.ldc = F;
   ga.role = zimg::ROLE_W13;
-  ga.split = split;
+  ga.split = gemm_split();
   PROFILED(K_W13, zimg::launch_gemm(ga, s));
 
   ga.A = g + (int64_t)r0 * F;
@@ -758,7 +793,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
   ga.role = zimg::ROLE_W2;
-  ga.split = split;
+  ga.split = gemm_split();
   PROFILED(K_W2, zimg::launch_gemm(ga, s));
 
   pn.w_post = w.fn2;
@@ -804,7 +839,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.K = P;
   ga.epi = zimg::EPI_F32_BIAS;
   ga.role = zimg::ROLE_EMBED;
-  ga.split = split;
+  ga.split = gemm_split();
   ga.ep.C = x;
   ga.ep.ldc = D;
   ga.ep.bias = x_b;
@@ -864,7 +899,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   ga.K = D;
   ga.epi = zimg::EPI_UNPATCH;
   ga.role = zimg::ROLE_FINAL;
-  ga.split = split;
+  ga.split = gemm_split();
   ga.ep.C = out;
   ga.ep.bias = fin_b;
   ga.ep.ntok = L.N;
@@ -1167,6 +1202,17 @@ int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stat
     stats[i].total_ms = h->prof.ms[i];
   }
   if (n_stats) *n_stats = zimg_dit::K_COUNT;
+  return ZIMG_OK;
+}
+
+int zimg_dit_attention_plan(zimg_dit* h, int32_t stage, int32_t out[3]) {
+  g_last_error.clear();
+  if (!h || !out) return set_err(ZIMG_EINVAL, "NULL argument");
+  if (stage < 0 || stage > 2) return set_err(ZIMG_EINVAL, "stage %d is not 0, 1 or 2", stage);
+  if (h->table_key.empty()) return set_err(ZIMG_ESTATE, "no forward has set a geometry yet");
+  out[0] = h->n_items_stage[stage] * h->cfg.n_heads;
+  out[1] = h->attn_full[stage];
+  out[2] = h->attn_split[stage];
   return ZIMG_OK;
 }
 

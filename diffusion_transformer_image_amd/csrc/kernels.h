@@ -124,6 +124,10 @@ struct AttnItem {
   int seg;
   int pad;
 };
+// Work units: the first n_full (item, head) pairs in logical order run whole;
+// each remaining pair is split into ``split`` chunks of its key tiles, whose
+// unnormalised outputs and (max, sum) go to ``part`` and are merged by a
+// second kernel in chunk order (deterministic).
 struct AttnArgs {
   const bf16_t* qkv;
   const bf16_t* vT;
@@ -132,7 +136,12 @@ struct AttnArgs {
   const AttnSeg* segs;
   int n_items, H, S_pad;
   float scale_log2;
+  int n_full;   // pairs computed whole (== n_items * H when nothing is split)
+  int split;    // chunks per remaining pair (1: none)
+  float* part;  // [units][128 q][128 d] fp32, then [units][128 q] (m, l)
 };
+// fp32 words of partial state one split unit needs
+constexpr int ATTN_PART_FLOATS = 128 * 128 + 2 * 128;
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- small ops

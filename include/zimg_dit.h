@@ -78,6 +78,12 @@ typedef struct zimg_dit_config {
   int32_t max_batch;         /* workspace sizing: samples per forward (1..64) */
   int32_t max_image_tokens;  /* per sample, (Hl/2)*(Wl/2) */
   int32_t max_caption_tokens;/* per sample, 1..512 */
+  int32_t batch_invariant;   /* 0 (default): the last, partial round of GEMM tiles and
+                                attention work is split along K / keys to fill the GPU,
+                                which makes the fp32 summation order depend on the whole
+                                batch; 1: no such splits, so each sample's result is
+                                bitwise the same whatever else is in the batch (slower
+                                when the last round is partial) */
 } zimg_dit_config;
 
 /* One named weight tensor handed to the engine.  ``data`` is a HOST

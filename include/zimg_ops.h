@@ -86,6 +86,19 @@ typedef struct zimg_kernel_stat {
 int zimg_dit_profile(zimg_dit* h, int32_t enable);
 int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
+/*
+ * Attention work decomposition chosen for one stage (0: noise refiner, the
+ * image rows; 1: context refiner, the caption rows; 2: joint blocks, all
+ * rows) at the geometry of the most recent forward or run_blocks call on the
+ * handle.  Work is one 128-query tile of one head (a "pair"); when the last
+ * round of resident workgroups would be at most half full, its pairs are
+ * each split into chunks of their 64-key tiles, merged afterwards.  HOST
+ * out[0] = pairs, out[1] = pairs computed whole, out[2] = chunks per other
+ * pair (1: none).  ZIMG_ESTATE before any call has set a geometry; ZIMG_EINVAL
+ * for a bad stage or NULL pointer.  For tests and measurement.
+ */
+int zimg_dit_attention_plan(zimg_dit* h, int32_t stage, int32_t out[3]);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,9 +16,9 @@ def oracle_config(model: dict) -> ModelConfig:
     return ModelConfig.from_dict(model)
 
 
-def engine_config(model: dict, max_batch=1, max_image_tokens=4096, max_caption_tokens=512):
+def engine_config(model: dict, max_batch=1, max_image_tokens=4096, max_caption_tokens=512, **extra):
     from diffusion_transformer_image_amd import binding
-    kw = dict(model)
+    kw = dict(model, **extra)
     return binding.config(max_batch=max_batch, max_image_tokens=max_image_tokens,
                           max_caption_tokens=max_caption_tokens, **kw)
 

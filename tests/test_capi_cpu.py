@@ -69,6 +69,7 @@ def test_full_manifest_counts():
     ("ffn", 100, "EUNSUPPORTED"),
     ("rope_axes", (32, 48, 40), "EUNSUPPORTED"),
     ("norm_eps", 0.0, "EINVAL"),
+    ("batch_invariant", 2, "EINVAL"),
 ])
 def test_config_validation(field, value, code):
     b = _b()

@@ -6,10 +6,10 @@ oracle cannot run 8 x 2 full-width forwards in a test); at full width and the
 workload's 1536x640 geometry the loop is checked for finiteness, bitwise
 reproducibility, and batch independence (each sample run alone matches its
 row of the batch to the parity bar; not bitwise: the batch size changes the
-GEMM tile counts and so which tiles are split along K, i.e. the fp32
-summation order, and after 8 x 34 blocks those last-bit differences have
-flipped enough bf16 roundings to reach ~2e-3.  With the split disabled the
-two are bitwise equal).
+GEMM tile counts and attention work items, and so which of them are split
+along K or keys, i.e. the fp32 summation order, and after 8 x 34 blocks
+those last-bit differences have flipped enough bf16 roundings to reach
+~2e-3.  The engine's batch-invariant option disables those splits).
 """
 
 import numpy as np
