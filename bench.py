@@ -55,18 +55,17 @@ def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
     bandwidth-bound classes, per forward, keyed by the engine's profile classes."""
     D, F = model["hidden"], model["ffn"]
     w = {k: 0.0 for k in ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
-                          "qknorm_rope", "pre_norm", "post_norm", "embed", "final_layer", "conditioning")}
+                          "pre_norm", "post_norm", "embed", "final_layer", "conditioning")}
     stages = stage_rows(model, n_img, lens)
     prev = None
     for i, (stage, rows) in enumerate(stages):
         M = sum(rows)
+        # (QK-RMSNorm + RoPE and the V transpose run in this GEMM's epilogue)
         w["gemm_qkv"] += 2.0 * M * D * 3 * D
         w["gemm_out"] += 2.0 * M * D * D
         w["gemm_w13_swiglu"] += 2.0 * M * D * 2 * F
         w["gemm_w2"] += 2.0 * M * F * D
         w["attention"] += sum(4.0 * r * r * D for r in rows)
-        # bytes: q,k read+write, v read + transposed write (bf16), RoPE tables (fp32 cos+sin)
-        w["qknorm_rope"] += M * (12.0 * D + 512)
         # pre-norm only where not fused into the previous block's last kernel
         if prev != stage:
             w["pre_norm"] += M * 6.0 * D
@@ -84,7 +83,7 @@ def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
 
 
 MFMA_CLASSES = ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention", "embed", "final_layer")
-HBM_CLASSES = ("qknorm_rope", "pre_norm", "post_norm")
+HBM_CLASSES = ("pre_norm", "post_norm")
 
 
 # ---------------------------------------------------------------- CPU baseline

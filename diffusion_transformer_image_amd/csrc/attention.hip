@@ -300,14 +300,28 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   }
   __syncthreads();
   const int D = a.H * HD;
-  for (int e = tid; e < it.nq * 32; e += 256) {
-    const int q = e >> 5, d = (e & 31) * 4;
-    f32x4 acc = {};
-    for (int c = 0; c < a.split; ++c) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(a.part + (int64_t)(c * n_rest + p) * (128 * HD) + q * HD + d);
-      acc += wt[c][q] * v;
+  // thread: float4 number tid + 256 k (k < 16) of the 128 x 128 tile, i.e.
+  // query (tid >> 5) + 8 k, dims (tid & 31) * 4 .. +3; chunk-outer so that a
+  // chunk's 16 loads are in flight together (queries past nq read finite
+  // but unused partials)
+  const int d = (tid & 31) * 4, q0 = tid >> 5;
+  f32x4 acc[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
+  for (int c = 0; c < a.split; ++c) {
+    const float* src = a.part + (int64_t)(c * n_rest + p) * (128 * HD) + q0 * HD + d;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int q = q0 + 8 * k;
+      const float w = q < it.nq ? wt[c][q] : 0.f;
+      acc[k] += w * *reinterpret_cast<const f32x4*>(src + 8 * k * HD);
     }
-    u32x2 u = {pack2bf(acc[0], acc[1]), pack2bf(acc[2], acc[3])};
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int q = q0 + 8 * k;
+    if (q >= it.nq) continue;
+    u32x2 u = {pack2bf(acc[k][0], acc[k][1]), pack2bf(acc[k][2], acc[k][3])};
     *reinterpret_cast<u32x2*>(a.out + (int64_t)(it.q0 + q) * D + h * HD + d) = u;
   }
 }

@@ -333,7 +333,7 @@ struct zimg_dit {
   std::vector<void*> allocations;
 
   // per-kernel-class timing with HIP events on the forward's stream
-  enum { K_QKV, K_OUT, K_W13, K_W2, K_ATTN, K_QKROPE, K_PRENORM, K_POSTNORM, K_EMBED, K_FINAL, K_COND, K_COUNT };
+  enum { K_QKV, K_OUT, K_W13, K_W2, K_ATTN, K_PRENORM, K_POSTNORM, K_EMBED, K_FINAL, K_COND, K_COUNT };
   struct Prof {
     bool on = false;
     std::vector<hipEvent_t> ev;  // pairs (start, stop)
@@ -721,15 +721,24 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.M = M;
   ga.N = 3 * D;
   ga.K = D;
-  ga.epi = zimg::EPI_BF16;
+  // epilogue: QK-RMSNorm + RoPE in place, V transposed into vT
+  ga.epi = zimg::EPI_QKV_ROPE;
   ga.ep.C = qkv + (int64_t)r0 * 3 * D;
   ga.ep.ldc = 3 * D;
+  ga.ep.wq = w.nq;
+  ga.ep.wk = w.nk;
+  ga.ep.cos_t = cos_t;
+  ga.ep.sin_t = sin_t;
+  ga.ep.vT = vT;
+  ga.ep.trow0 = r0;
+  ga.ep.S_pad = (int)S_pad;
+  ga.ep.D = D;
+  ga.ep.eps = c.norm_eps;
   ga.role = zimg::ROLE_QKV;
   ga.split = gemm_split();
   PROFILED(K_QKV, zimg::launch_gemm(ga, s));
-
-  zimg::QKRopeArgs qa{qkv, vT, w.nq, w.nk, cos_t, sin_t, r0, r1, H, (int)S_pad, c.norm_eps};
-  PROFILED(K_QKROPE, zimg::launch_qknorm_rope(qa, s));
+  ga.ep = zimg::EpiArgs{};
+  ga.epi = zimg::EPI_BF16;
 
   zimg::AttnArgs aa{qkv,
                     vT,
@@ -1156,7 +1165,8 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
   g.ep.ldc = ldc;
   g.ep.bias = bias;
   g.role = zimg::ROLE_ANY;
-  if (epilogue == zimg::EPI_UNPATCH) return set_err(ZIMG_EUNSUPPORTED, "the unpatchify epilogue is internal");
+  if (epilogue == zimg::EPI_UNPATCH || epilogue == zimg::EPI_QKV_ROPE)
+    return set_err(ZIMG_EUNSUPPORTED, "epilogue %d is internal", epilogue);
   if (const char* m = zimg::gemm_check(g)) return set_err(ZIMG_EINVAL, "%s", m);
   const int64_t need = epilogue == zimg::EPI_SWIGLU ? N / 2 : N;
   if (ldc < need) return set_err(ZIMG_EINVAL, "ldc %lld smaller than the output width %lld", (long long)ldc, (long long)need);
@@ -1189,7 +1199,7 @@ int zimg_dit_profile(zimg_dit* h, int32_t enable) {
 
 int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats) {
   static const char* names[zimg_dit::K_COUNT] = {"gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
-                                                 "qknorm_rope", "pre_norm", "post_norm", "embed", "final_layer",
+                                                 "pre_norm", "post_norm", "embed", "final_layer",
                                                  "conditioning"};
   g_last_error.clear();
   if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");

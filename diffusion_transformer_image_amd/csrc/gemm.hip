@@ -20,7 +20,8 @@
 // of w3) and the output is silu(a1) * a3 (the SwiGLU FFN of "Z-Image" (AI
 // Toolkit docs), Architecture); and the final-layer scatter back to the
 // [B, C, Hl, Wl] latent with bias (unpatchify of 2x2 patches, "Latent
-// space").
+// space"); and the QKV projection's QK-RMSNorm + 3-axis RoPE + V transpose
+// ("Z-Image" (AI Toolkit docs), Architecture: QK RMSNorm and 3D RoPE).
 #include "common.h"
 #include "kernels.h"
 
@@ -91,6 +92,127 @@ __device__ __forceinline__ void epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 3
           }
         }
       }
+  }
+}
+
+// One 16-lane group's share of a (row, head) of q or k: lane k holds the
+// head's values 8k .. 8k+7 (bf16 pairs in x), i.e. RoPE pairs 4k .. 4k+3.
+// RMS over the group, weight, rotation by the row's table, 16-byte store
+// (only if ``store``).  All 16 lanes of the group must be active.
+ZI_DEV void qk_rope_unit(const u32x4& x, int k, const float (&wv)[8], float eps, const float* cos_row,
+                         const float* sin_row, bf16_t* dst, bool store) {
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = __uint_as_float(x[q] << 16), b = __uint_as_float(x[q] & 0xffff0000u);
+    ss = fmaf(a, a, ss);
+    ss = fmaf(b, b, ss);
+  }
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  ss += __shfl_xor(ss, 8, 64);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+  const float4 cc = *reinterpret_cast<const float4*>(cos_row + k * 4);
+  const float4 sc = *reinterpret_cast<const float4*>(sin_row + k * 4);
+  const float cv[4] = {cc.x, cc.y, cc.z, cc.w}, sv[4] = {sc.x, sc.y, sc.z, sc.w};
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = __uint_as_float(x[q] << 16) * inv * wv[2 * q];
+    const float b = __uint_as_float(x[q] & 0xffff0000u) * inv * wv[2 * q + 1];
+    o[q] = pack2bf(a * cv[q] - b * sv[q], a * sv[q] + b * cv[q]);
+  }
+  if (store) *reinterpret_cast<u32x4*>(dst + k * 8) = o;
+}
+
+ZI_DEV void qk_weights(const EpiArgs& ep, int sec, int k, float (&wv)[8]) {
+  const float* w = sec ? ep.wk : ep.wq;
+  const float4 wa = *reinterpret_cast<const float4*>(w + k * 8);
+  const float4 wb = *reinterpret_cast<const float4*>(w + k * 8 + 4);
+  wv[0] = wa.x, wv[1] = wa.y, wv[2] = wa.z, wv[3] = wa.w, wv[4] = wb.x, wv[5] = wb.y, wv[6] = wb.z, wv[7] = wb.w;
+}
+
+// Fused epilogue of the QKV projection, 256 x 256 tiles of 8 waves (2 x 4).
+// Hidden is a multiple of 256, so a tile lies inside one of the q, k, v
+// column blocks and covers two heads.  The tile, rounded to bf16, is staged
+// in LDS (the four 32 KB operand buffers, 64 rows or columns each), then:
+//  - q, k: 16 lanes per (row, head) RMS-normalise the head's 128 values
+//    (weight wq or wk), rotate pair (2p, 2p+1) by the row's table entry p,
+//    and store the head back in place;
+//  - v: 16-byte runs of 8 rows of one column are stored into the transposed
+//    copy vT[head*128 + d][row].
+// Staging layouts keep LDS accesses free of bank conflicts: q/k rows of
+// 512 B hold their 16-byte chunk c at position c ^ (r & 15); v columns of
+// 512 B (256 rows) hold chunk k (rows 8k..8k+7) at position k ^ (col & 15).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0,
+                                                  int M, const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2,
+                                                  bf16_t* s3) {
+  static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "QKV epilogue tiling");
+  constexpr int TM = 4, TN = 2;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int sec = n0 / ep.D;  // 0: q, 1: k, 2: v
+  auto region = [&](int k) { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
+  __syncthreads();  // every wave has finished reading the operand buffers
+  if (sec < 2) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      bf16_t* rg = region(wm * 2 + (i >> 1));
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn * 64 + j * 32 + lrow;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+          rg[(r & 63) * 256 + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f2bf(acc[i][j][e]);
+        }
+      }
+    }
+    __syncthreads();
+    // 16 lanes per (row, head), so table reads and stores are 256-byte runs;
+    // rows past M are computed from a clamped table row and not stored
+    const int k = lane & 15;
+    float wv[8];
+    qk_weights(ep, sec, k, wv);
+    bf16_t* C = reinterpret_cast<bf16_t*>(ep.C);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int u = p * 32 + wid * 4 + (lane >> 4);  // (row, head) unit
+      const int r = u >> 1, hl = u & 1;               // r >> 6 == p >> 2
+      const u32x4 x = *reinterpret_cast<const u32x4*>(region(p >> 2) + (r & 63) * 256 + (((hl * 16 + k) ^ (r & 15)) << 3));
+      const int row = m0 + r;
+      const int64_t trow = (int64_t)ep.trow0 + min(row, M - 1);
+      qk_rope_unit(x, k, wv, ep.eps, ep.cos_t + trow * 64, ep.sin_t + trow * 64,
+                   C + (int64_t)row * ep.ldc + n0 + hl * 128, row < M);
+    }
+  } else {
+    bf16_t* rg = region(wn);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = j * 32 + lrow;  // within the wave's 64 columns = the region's
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int k = wm * 16 + i * 4 + g;  // 8-row chunk
+          const u32x2 v = {pack2bf(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]),
+                           pack2bf(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3])};
+          *reinterpret_cast<u32x2*>(rg + col * 256 + ((k ^ (col & 15)) << 3) + lhalf * 4) = v;
+        }
+      }
+    __syncthreads();
+    const int vcol0 = n0 - 2 * ep.D;  // head*128 + d of the tile's first column
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int unit = u * 512 + tid, k = unit & 31, c = unit >> 5;
+      const int r = k * 8;
+      if (m0 + r >= M) continue;  // stage row counts are multiples of 8
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region(u >> 2) + (c & 63) * 256 + ((k ^ (c & 15)) << 3));
+      *reinterpret_cast<u32x4*>(ep.vT + (int64_t)(vcol0 + c) * ep.S_pad + ep.trow0 + m0 + r) = v;
+    }
   }
 }
 
@@ -240,7 +362,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
         for (int e = 0; e < 16; ++e) part[((i * TN + j) * 16 + e) * NT + tid] = acc[i][j][e];
     return;
   }
-  epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
+  if constexpr (EPI == EPI_QKV_ROPE)
+    qkv_rope_epilogue<BM, BN, WM, WN>(acc, m0, n0, M, ep, As0, Bs0, As1, Bs1);
+  else
+    epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
 }
 
 // Sum of the nsplit partials of each split tile, in chunk order (so the
@@ -267,34 +392,42 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
   const int m0 = (first_m + (lid % per_group) % gsize) * BM;
   const int n0 = ((lid % per_group) / gsize) * BN;
   const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F;
+  int qs[RED_PER_THREAD];
 #pragma unroll
   for (int r = 0; r < RED_PER_THREAD; ++r) {
     const int slot = (blockIdx.x % WG_PER_TILE) * PER_WG + r * 256 + threadIdx.x;
     // slot -> accumulator index q (SwiGLU: the w1 half, j even)
-    int q = slot;
+    qs[r] = slot;
     if constexpr (EPI == EPI_SWIGLU) {
       const int tid_ = slot % NT, rest = slot / NT;  // rest = (i*(TN/2) + jp)*16 + e
       const int e = rest % 16, ijp = rest / 16, jp = ijp % (TN / 2), i = ijp / (TN / 2);
-      q = ((i * TN + 2 * jp) * 16 + e) * NT + tid_;
+      qs[r] = ((i * TN + 2 * jp) * 16 + e) * NT + tid_;
     }
+  }
+  // chunk-outer, so that all of a chunk's loads are in flight together
+  float v[RED_PER_THREAD] = {}, v3[RED_PER_THREAD] = {};
+  for (int c = 0; c < nsplit; ++c, part += TILE_F)
+#pragma unroll
+    for (int r = 0; r < RED_PER_THREAD; ++r) {
+      v[r] += part[qs[r]];
+      if constexpr (EPI == EPI_SWIGLU) v3[r] += part[qs[r] + 16 * NT];
+    }
+#pragma unroll
+  for (int r = 0; r < RED_PER_THREAD; ++r) {
+    const int q = qs[r];
     const int tid_ = q % NT, e = (q / NT) % 16, ij = q / NT / 16, j = ij % TN, i = ij / TN;
     const int wid = tid_ >> 6, lane = tid_ & 63, wm = wid / WN, wn = wid % WN;
     const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
     const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-    float v = 0.f, v3 = 0.f;
-    for (int c = 0; c < nsplit; ++c) {
-      v += part[(int64_t)c * TILE_F + q];
-      if constexpr (EPI == EPI_SWIGLU) v3 += part[(int64_t)c * TILE_F + q + 16 * NT];
-    }
     if (row >= M || col >= N) continue;
     if constexpr (EPI == EPI_SWIGLU) {
-      const float s = v / (1.0f + __expf(-v));
+      const float s = v[r] / (1.0f + __expf(-v[r]));
       const int ocol = ((n0 + wn * WTN + j * 32) >> 1) + (lane & 31);
-      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + ocol] = f2bf(s * v3);
+      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + ocol] = f2bf(s * v3[r]);
     } else if constexpr (EPI == EPI_BF16) {
-      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + col] = f2bf(v);
+      reinterpret_cast<bf16_t*>(ep.C)[(int64_t)row * ep.ldc + col] = f2bf(v[r]);
     } else if constexpr (EPI == EPI_F32_BIAS) {
-      reinterpret_cast<float*>(ep.C)[(int64_t)row * ep.ldc + col] = v + (ep.bias ? ep.bias[col] : 0.f);
+      reinterpret_cast<float*>(ep.C)[(int64_t)row * ep.ldc + col] = v[r] + (ep.bias ? ep.bias[col] : 0.f);
     } else {
       const int b = row / ep.npad, n = row - b * ep.npad;
       if (n >= ep.ntok) continue;
@@ -303,7 +436,82 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
       const int pa = ab / ep.patch, pb = ab - pa * ep.patch;
       const int Hl = ep.Hp * ep.patch, Wl = ep.Wp * ep.patch;
       reinterpret_cast<float*>(ep.C)[(((int64_t)b * ep.C_ch + ch) * Hl + pi * ep.patch + pa) * Wl + pj * ep.patch +
-                                     pb] = v + (ep.bias ? ep.bias[col] : 0.f);
+                                     pb] = v[r] + (ep.bias ? ep.bias[col] : 0.f);
+    }
+  }
+}
+
+// Split tiles of the QKV projection: a workgroup of 256 threads per 32-row
+// slice of a split tile (slice = (wm, i) of the producing kernel's layout;
+// thread (wn, lane) takes over that wave's accumulators of the slice) sums
+// the partials in chunk order, then runs the epilogue on the slice: q / k
+// rows staged in LDS (same swizzle as the tile epilogue) and handed to
+// qk_rope_unit; v written transposed straight from the registers (lanes
+// l and l + 32 hold 4 + 4 consecutive rows of one column).
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void gemm_qkv_reduce_kernel(int M, EpiArgs ep, int tiles_m, int tiles_n,
+                                                              int full_tiles, int nsplit, const float* __restrict__ ws) {
+  static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "QKV epilogue tiling");
+  constexpr int TM = 4, TN = 2, TILE_F = BM * BN;
+  __shared__ __attribute__((aligned(16))) bf16_t st[32 * 256];
+  const int tail_idx = blockIdx.x >> 3, slice = blockIdx.x & 7;
+  const int wm = slice >> 2, i = slice & 3;  // rows wm*128 + i*32 .. +31 of the tile
+  const int lid = full_tiles + tail_idx;
+  const int per_group = GROUP_M * tiles_n;
+  const int first_m = (lid / per_group) * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int m0 = (first_m + (lid % per_group) % gsize) * BM;
+  const int n0 = ((lid % per_group) / gsize) * BN;
+  const int tid = threadIdx.x, wn = tid >> 6, lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
+  const int src_tid = (wm * WN + wn) * 64 + lane;
+  const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F + src_tid;
+  f32x16 acc[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) acc[j] = f32x16{};
+  for (int c = 0; c < nsplit; ++c, part += TILE_F)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[j][e] += part[((i * TN + j) * 16 + e) * NT];
+  const int sec = n0 / ep.D;
+  const int rs0 = wm * 128 + i * 32;  // slice's first row in the tile
+  if (sec < 2) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * 64 + j * 32 + lrow;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = (e >> 2) * 8 + lhalf * 4 + (e & 3);
+        st[r * 256 + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f2bf(acc[j][e]);
+      }
+    }
+    __syncthreads();
+    const int k = lane & 15;
+    float wv[8];
+    qk_weights(ep, sec, k, wv);
+    bf16_t* C = reinterpret_cast<bf16_t*>(ep.C);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int u = p * 16 + (tid >> 4);  // (row, head) unit of the slice
+      const int r = u >> 1, hl = u & 1;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(st + r * 256 + (((hl * 16 + k) ^ (r & 15)) << 3));
+      const int row = m0 + rs0 + r;
+      const int64_t trow = (int64_t)ep.trow0 + min(row, M - 1);
+      qk_rope_unit(x, k, wv, ep.eps, ep.cos_t + trow * 64, ep.sin_t + trow * 64,
+                   C + (int64_t)row * ep.ldc + n0 + hl * 128, row < M);
+    }
+  } else {
+    const int vcol0 = n0 - 2 * ep.D;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = wn * 64 + j * 32 + lrow;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = m0 + rs0 + g * 8 + lhalf * 4;
+        if (row >= M) continue;  // stage row counts are multiples of 8
+        const u32x2 v = {pack2bf(acc[j][g * 4 + 0], acc[j][g * 4 + 1]), pack2bf(acc[j][g * 4 + 2], acc[j][g * 4 + 3])};
+        *reinterpret_cast<u32x2*>(ep.vT + (int64_t)(vcol0 + col) * ep.S_pad + ep.trow0 + row) = v;
+      }
     }
   }
 }
@@ -346,6 +554,11 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
                      g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
+  if constexpr (EPI == EPI_QKV_ROPE) {
+    hipLaunchKernelGGL((gemm_qkv_reduce_kernel<BM, BN, WM, WN>), dim3((T - full) * 8), dim3(256), 0, s, g.M, g.ep,
+                       tiles_m, tiles_n, full, nsplit, g.split.ws);
+    return hipGetLastError();
+  }
   constexpr int SLOTS = (EPI == EPI_SWIGLU) ? BM * BN / 2 : BM * BN;
   static_assert(SLOTS % (256 * RED_PER_THREAD) == 0, "reduce grid");
   hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WM, WN, EPI>), dim3((T - full) * (SLOTS / (256 * RED_PER_THREAD))),
@@ -372,8 +585,12 @@ const char* gemm_check(const GemmArgs& g) {
   if (!g.A || !g.W || !g.ep.C) return "gemm: null pointer";
   if (g.epi == EPI_UNPATCH && (g.ep.ntok <= 0 || g.ep.npad < g.ep.ntok || g.ep.Wp <= 0 || g.ep.C_ch <= 0 || g.ep.patch <= 0))
     return "gemm: bad unpatchify geometry";
-  if (g.epi < 0 || g.epi > EPI_UNPATCH) return "gemm: unknown epilogue";
-  if ((g.role == ROLE_QKV && (g.epi != EPI_BF16 || g.N % 256)) || (g.role == ROLE_W13 && g.epi != EPI_SWIGLU) ||
+  if (g.epi < 0 || g.epi > EPI_QKV_ROPE) return "gemm: unknown epilogue";
+  if (g.epi == EPI_QKV_ROPE &&
+      (g.N != 3 * g.ep.D || g.ep.D % 256 || g.M % 8 || !g.ep.wq || !g.ep.wk || !g.ep.cos_t || !g.ep.sin_t ||
+       !g.ep.vT || g.ep.trow0 < 0 || g.ep.trow0 % 8 || g.ep.S_pad < g.ep.trow0 + g.M || g.ep.S_pad % 8))
+    return "gemm: bad QKV epilogue arguments";
+  if ((g.role == ROLE_QKV) != (g.epi == EPI_QKV_ROPE) || (g.role == ROLE_W13 && g.epi != EPI_SWIGLU) ||
       ((g.role == ROLE_OUT || g.role == ROLE_W2) && g.epi != EPI_BF16) ||
       (g.role == ROLE_EMBED && g.epi != EPI_F32_BIAS) || (g.role == ROLE_FINAL && g.epi != EPI_UNPATCH))
     return "gemm: role and epilogue disagree";
@@ -382,7 +599,7 @@ const char* gemm_check(const GemmArgs& g) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   switch (g.role) {
-    case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_BF16, ROLE_QKV>(g, s);
+    case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_QKV_ROPE, ROLE_QKV>(g, s);
     case ROLE_OUT: return launch_epi<EPI_BF16, ROLE_OUT>(g, s);
     case ROLE_W13: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_W13>(g, s);
     case ROLE_W2: return launch_epi<EPI_BF16, ROLE_W2>(g, s);

@@ -11,7 +11,7 @@
 namespace zimg {
 
 // ---------------------------------------------------------------- GEMM
-enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_SWIGLU = 2, EPI_UNPATCH = 3 };
+enum { EPI_BF16 = 0, EPI_F32_BIAS = 1, EPI_SWIGLU = 2, EPI_UNPATCH = 3, EPI_QKV_ROPE = 4 };
 // which projection a launch is (selects the kernel symbol and tile shape)
 enum { ROLE_ANY = 0, ROLE_QKV = 1, ROLE_OUT = 2, ROLE_W13 = 3, ROLE_W2 = 4, ROLE_EMBED = 5, ROLE_FINAL = 6 };
 
@@ -23,6 +23,17 @@ struct EpiArgs {
   // sample b (rows with n >= ntok are alignment padding and are skipped),
   // GEMM column = (a*patch + b)*C_ch + ch; output [B, C_ch, Hp*patch, Wp*patch]
   int ntok, npad, Hp, Wp, C_ch, patch;
+  // QKV_ROPE (C = the qkv buffer, width 3*D): q and k of every head are
+  // RMS-normalised over 128 (weights wq, wk) and rotated by the row's table
+  // (cos_t / sin_t [rows, 64], table row = trow0 + GEMM row) in place; v is
+  // written transposed to vT[head*128 + d][trow0 + GEMM row] (row stride S_pad)
+  const float* wq;
+  const float* wk;
+  const float* cos_t;
+  const float* sin_t;
+  bf16_t* vT;
+  int trow0, S_pad, D;
+  float eps;
 };
 
 // Split of the last, partial wave of tiles along K (see gemm.hip): null
@@ -97,21 +108,6 @@ hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s);
 hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t* out,
                                int rows, int Dc, float eps, hipStream_t s);
 
-// ---------------------------------------------------------------- QK norm + RoPE
-// qkv rows [r0, r1) of width 3*D: q and k heads RMS-normalised over 128
-// (weights wq, wk) and rotated by the row's table (cos/sin [S, 64]) in place;
-// v written transposed to vT[h][d][row] (row stride S_pad).
-struct QKRopeArgs {
-  bf16_t* qkv;
-  bf16_t* vT;
-  const float* wq;
-  const float* wk;
-  const float* cos_t;
-  const float* sin_t;
-  int r0, r1, H, S_pad;
-  float eps;
-};
-hipError_t launch_qknorm_rope(const QKRopeArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- attention
 struct AttnSeg {

@@ -1,9 +1,10 @@
 // HBM-bound row kernels of the S3-DiT block: the adaLN-modulated pre-norm,
 // the fused post-norm + tanh gate + residual (+ the next pre-norm), the
-// caption RMSNorm, QK-RMSNorm + 3-axis RoPE with the V transpose, patchify.
+// caption RMSNorm, patchify.  (QK-RMSNorm + RoPE is fused into the QKV
+// projection's epilogue.)
 //
 // Block structure ("Z-Image" (AI Toolkit docs), Architecture: RMSNorm,
-// QK RMSNorm, adaLN from the timestep embedding; "Z-Image-Turbo MNN (int8,
+// adaLN from the timestep embedding; "Z-Image-Turbo MNN (int8,
 // fp16-safe)", Conversion details: the to_out and w2 outputs feed an
 // RMSNorm).  Residual rows are fp32 and every reduction is fp32; activations
 // handed to the GEMMs are bf16.
@@ -155,60 +156,6 @@ __global__ __launch_bounds__(256) void rows_rmsnorm_kernel(const void* x, const 
     }
 }
 
-// QK-RMSNorm + RoPE for a tile of 64 rows of one head, plus the V transpose.
-// Lane p of a wave owns channel pair (2p, 2p+1) of a 128-wide head, which is
-// exactly RoPE pair p, so the rotation needs no data exchange.
-constexpr int QK_ROWS = 64;
-constexpr int VPAD = 136;  // LDS row stride (bf16) of the V staging tile
-
-__global__ __launch_bounds__(256) void qknorm_rope_kernel(QKRopeArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t vs[QK_ROWS * VPAD];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.y;
-  const int rt0 = a.r0 + blockIdx.x * QK_ROWS;
-  const int D = a.H * 128;
-  const int64_t ld = 3 * (int64_t)D;
-  const float wq0 = a.wq[2 * lane], wq1 = a.wq[2 * lane + 1];
-  const float wk0 = a.wk[2 * lane], wk1 = a.wk[2 * lane + 1];
-
-  for (int rr = wave; rr < QK_ROWS; rr += 4) {
-    const int r = rt0 + rr;
-    if (r >= a.r1) break;
-    const float c = a.cos_t[(int64_t)r * 64 + lane], s = a.sin_t[(int64_t)r * 64 + lane];
-#pragma unroll
-    for (int part = 0; part < 2; ++part) {
-      uint32_t* p = reinterpret_cast<uint32_t*>(a.qkv + r * ld + part * D + h * 128) + lane;
-      const uint32_t u = *p;
-      const float x0 = __uint_as_float(u << 16), x1 = __uint_as_float(u & 0xffff0000u);
-      const float inv = 1.0f / sqrtf(wave_sum(x0 * x0 + x1 * x1) * (1.0f / 128.0f) + a.eps);
-      const float n0 = x0 * inv * (part ? wk0 : wq0);
-      const float n1 = x1 * inv * (part ? wk1 : wq1);
-      *p = pack2bf(n0 * c - n1 * s, n0 * s + n1 * c);
-    }
-  }
-
-  // V tile -> LDS (rows past r1 are zero so the transposed copy stays finite)
-  for (int i = 0; i < 4; ++i) {
-    const int cidx = threadIdx.x + 256 * i, row = cidx >> 4, ch = cidx & 15;
-    const int r = rt0 + row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < a.r1) v = *reinterpret_cast<const u32x4*>(a.qkv + r * ld + 2 * D + h * 128 + ch * 8);
-    *reinterpret_cast<u32x4*>(&vs[row * VPAD + ch * 8]) = v;
-  }
-  __syncthreads();
-  // vT[h][d][rt0 + 8*rc .. +8]: 128 d-rows x 8 chunks of 8 rows
-  for (int i = 0; i < 4; ++i) {
-    const int cidx = threadIdx.x + 256 * i, d = cidx >> 3, rc = cidx & 7;
-    if (rt0 + rc * 8 >= a.r1) continue;  // stage bounds are multiples of 8
-    uint32_t w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      w[u] = (uint32_t)vs[(rc * 8 + 2 * u) * VPAD + d] | ((uint32_t)vs[(rc * 8 + 2 * u + 1) * VPAD + d] << 16);
-    u32x4 o = {w[0], w[1], w[2], w[3]};
-    *reinterpret_cast<u32x4*>(a.vT + ((int64_t)(h * 128 + d)) * a.S_pad + rt0 + rc * 8) = o;
-  }
-}
-
 __global__ void patchify_kernel(const float* lat, bf16_t* out, int B, int C, int Hp, int Wp, int p,
                                 int npad) {
   const int64_t F = (int64_t)p * p * C;
@@ -248,13 +195,6 @@ hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t
     hipLaunchKernelGGL(rows_rmsnorm_kernel<true>, dim3((rows + 3) / 4), dim3(256), 0, s, x, w, out, rows, Dc, eps);
   else
     hipLaunchKernelGGL(rows_rmsnorm_kernel<false>, dim3((rows + 3) / 4), dim3(256), 0, s, x, w, out, rows, Dc, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_qknorm_rope(const QKRopeArgs& a, hipStream_t s) {
-  const int rows = a.r1 - a.r0;
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(qknorm_rope_kernel, dim3((rows + QK_ROWS - 1) / QK_ROWS, a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -72,8 +72,9 @@ int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void*
  * event pool once and resets the totals; zimg_dit_profile(h, 0) stops
  * recording.  zimg_dit_profile_read() waits for recorded events and writes
  * up to max_stats entries (name, launches, total milliseconds); *n_stats
- * receives the number of classes.  Classes: gemm_qkv, gemm_out,
- * gemm_w13_swiglu, gemm_w2, attention, qknorm_rope, pre_norm, post_norm,
+ * receives the number of classes.  Classes: gemm_qkv (with QK-RMSNorm,
+ * RoPE and the V transpose in its epilogue), gemm_out,
+ * gemm_w13_swiglu, gemm_w2, attention, pre_norm, post_norm,
  * embed (patchify + caption norm + both embed GEMMs), final_layer,
  * conditioning (timestep MLP + the adaLN projection).
  */
