@@ -302,8 +302,8 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   const int D = a.H * HD;
   // thread: float4 number tid + 256 k (k < 16) of the 128 x 128 tile, i.e.
   // query (tid >> 5) + 8 k, dims (tid & 31) * 4 .. +3; chunk-outer so that a
-  // chunk's 16 loads are in flight together (queries past nq read finite
-  // but unused partials)
+  // chunk's 16 loads are in flight together (queries past nq combine stale
+  // workspace values with weight 0 and are never stored)
   const int d = (tid & 31) * 4, q0 = tid >> 5;
   f32x4 acc[16];
 #pragma unroll

@@ -305,6 +305,12 @@ struct zimg_dit {
   bf16_t *h = nullptr, *qkv = nullptr, *vT = nullptr, *o = nullptr, *y = nullptr, *g = nullptr, *xin = nullptr,
          *capn = nullptr;
   float *temb = nullptr, *hmid = nullptr, *cvec = nullptr, *mod = nullptr;
+  // the blocks' four norm weights, [n_blocks][4][D] (an1, an2, fn1, fn2), and
+  // per forward those weights with the sample's modulation folded in,
+  // [max_batch][4 n_blocks + 1][D] (the last slot: the final layer's 1 + s)
+  float *normw = nullptr, *fold = nullptr;
+  int32_t* mod_idx_d = nullptr;
+  int64_t fold_stride = 0;
   float *cos_t = nullptr, *sin_t = nullptr;
   int32_t* row_sample = nullptr;
   zimg::AttnSeg* segs = nullptr;    // [3][max_batch]
@@ -417,6 +423,12 @@ int zimg_dit::allocate() {
   int rc;
 #define ALLOC(p, n) \
   if ((rc = dalloc(&(p), (size_t)(n))) != ZIMG_OK) return rc
+  const int64_t nb = (int64_t)blocks.size();
+  ALLOC(normw, nb * 4 * D);
+  ALLOC(mod_idx_d, nb);
+  HIP_TRY(hipMemcpy(mod_idx_d, mod_index.data(), nb * sizeof(int32_t), hipMemcpyHostToDevice));
+  fold_stride = (4 * nb + 1) * D;
+  ALLOC(fold, (int64_t)c.max_batch * fold_stride);
   ALLOC(t1w, (int64_t)c.t_mid * c.adaln_dim);
   ALLOC(t1b, c.t_mid);
   ALLOC(t2w, (int64_t)c.adaln_dim * c.t_mid);
@@ -438,10 +450,10 @@ int zimg_dit::allocate() {
     ALLOC(w.wo, D * D);
     ALLOC(w.w13, 2 * F * D);
     ALLOC(w.w2, D * F);
-    ALLOC(w.an1, D);
-    ALLOC(w.an2, D);
-    ALLOC(w.fn1, D);
-    ALLOC(w.fn2, D);
+    w.an1 = normw + (int64_t)(4 * i + 0) * D;
+    w.an2 = normw + (int64_t)(4 * i + 1) * D;
+    w.fn1 = normw + (int64_t)(4 * i + 2) * D;
+    w.fn2 = normw + (int64_t)(4 * i + 3) * D;
     ALLOC(w.nq, 128);
     ALLOC(w.nk, 128);
   }
@@ -685,6 +697,7 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
                               L.B, 0, s));
   HIP_TRY(zimg::launch_gemv(ada_w + n_mod * 4 * D * c.adaln_dim, ada_b + n_mod * 4 * D, cvec, c.adaln_dim,
                             mod + n_mod * 4 * D, mod_stride, (int)D, c.adaln_dim, L.B, 1, s));
+  HIP_TRY(zimg::launch_fold_mod(mod, mod_stride, normw, mod_idx_d, (int)blocks.size(), n_mod, (int)D, L.B, fold, s));
   return prof_stop(s);
 }
 
@@ -705,12 +718,11 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   int r0, r1;
   stage_rows(L, stage, r0, r1);
   const int M = r1 - r0;
-  const int mi = mod_index[bi];
-  auto mref = [&](int chunk) {
-    return mi < 0 ? zimg::ModRef{nullptr, 0, 0} : zimg::ModRef{mod, mod_stride, (int)(mi * 4 * D + chunk * D)};
-  };
+  // folded norm weights of this block: 0 attention pre, 1 attention post,
+  // 2 FFN pre, 3 FFN post
+  auto mref = [&](int chunk) { return zimg::VecRef{fold + (int64_t)(4 * bi + chunk) * D, fold_stride}; };
   if (!h_ready) {
-    zimg::PreNormArgs pa{x, w.an1, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0};
+    zimg::PreNormArgs pa{x, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0};
     PROFILED(K_PRENORM, zimg::launch_pre_norm(pa, s));
   }
   zimg::GemmArgs ga{};
@@ -766,14 +778,12 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   zimg::PostNormArgs pn{};
   pn.x = x;
   pn.y = y;
-  pn.w_post = w.an2;
-  pn.gate = mref(1);
+  pn.wg = mref(1);
   pn.r0 = r0;
   pn.r1 = r1;
   pn.n0 = r0;
   pn.n1 = r1;
-  pn.w_next = w.fn1;
-  pn.scale_next = mref(2);
+  pn.wn = mref(2);
   pn.next_kind = 0;
   pn.next_eps = c.norm_eps;
   pn.row_sample = row_sample;
@@ -805,20 +815,15 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.split = gemm_split();
   PROFILED(K_W2, zimg::launch_gemm(ga, s));
 
-  pn.w_post = w.fn2;
-  pn.gate = mref(3);
+  pn.wg = mref(3);
   if (next == 1) {
-    const int ni = bi + 1;
-    const int nmi = mod_index[ni];
-    pn.w_next = bw[ni].an1;
-    pn.scale_next = nmi < 0 ? zimg::ModRef{nullptr, 0, 0} : zimg::ModRef{mod, mod_stride, (int)(nmi * 4 * D)};
+    pn.wn = zimg::VecRef{fold + (int64_t)(4 * (bi + 1)) * D, fold_stride};
     pn.next_kind = 0;
     pn.next_eps = c.norm_eps;
   } else if (next == 2) {
     pn.n0 = 0;
     pn.n1 = L.cap_base;
-    pn.w_next = nullptr;
-    pn.scale_next = zimg::ModRef{mod, mod_stride, (int)(n_mod * 4 * D)};
+    pn.wn = zimg::VecRef{fold + (int64_t)(4 * blocks.size()) * D, fold_stride};
     pn.next_kind = 1;
     pn.next_eps = c.final_eps;
   } else {
@@ -893,7 +898,7 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
   rc = prof_start(K_FINAL, s);
   if (rc) return rc;
   if (!final_ready) {
-    zimg::PreNormArgs pa{x, nullptr, zimg::ModRef{mod, mod_stride, (int)(n_mod * 4 * D)}, row_sample, h, 0,
+    zimg::PreNormArgs pa{x, zimg::VecRef{fold + (int64_t)(4 * blocks.size()) * D, fold_stride}, row_sample, h, 0,
                          L.cap_base, D, c.final_eps, 1};
     HIP_TRY(zimg::launch_pre_norm(pa, s));
   }

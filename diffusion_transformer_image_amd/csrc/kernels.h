@@ -62,20 +62,19 @@ const char* gemm_check(const GemmArgs& g);  // null if OK
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 
 // ---------------------------------------------------------------- norms
-// Modulation vectors: mod[sample * mod_stride + off + d], fp32.  A null
-// ``mod`` means unmodulated (scale 1, gate 1).
-struct ModRef {
-  const float* mod;
+// A per-sample fp32 vector v[sample * stride + d]: a norm weight with its
+// modulation folded in (weight * (1 + scale), weight * tanh(gate), or the
+// final layer's 1 + scale), written once per forward by fold_mod.
+struct VecRef {
+  const float* v;
   int64_t stride;
-  int off;
 };
 
-// h[r] = bf16( N(x[r]) * (1 + scale) ) for rows r in [r0, r1), with
-// N = RMSNorm with weight w (kind 0) or LayerNorm without affine (kind 1).
+// h[r] = bf16( N(x[r]) * w[sample(r)] ) for rows r in [r0, r1), with N the
+// unit RMSNorm (kind 0) or the LayerNorm without affine (kind 1).
 struct PreNormArgs {
   const float* x;
-  const float* w;
-  ModRef scale;
+  VecRef w;
   const int32_t* row_sample;
   bf16_t* h;
   int r0, r1, D;
@@ -84,17 +83,16 @@ struct PreNormArgs {
 };
 hipError_t launch_pre_norm(const PreNormArgs& a, hipStream_t s);
 
-// For rows r in [r0, r1):  x[r] += gate * RMSNorm(y[r]; w_post), gate =
-// tanh(g) or 1; then, for rows in [n0, n1), h[r] = bf16(N_next(x[r]) * (1 + scale_next)).
+// For rows r in [r0, r1):  x[r] += RMSNorm_unit(y[r]) * wg[sample(r)]  (wg =
+// post-norm weight * gate); then, for rows in [n0, n1),
+// h[r] = bf16(N_next(x[r]) * wn[sample(r)]).
 struct PostNormArgs {
   float* x;
   const bf16_t* y;
-  const float* w_post;
-  ModRef gate;
+  VecRef wg;
   int r0, r1;
   int n0, n1;  // n0 >= n1: no next norm
-  const float* w_next;
-  ModRef scale_next;
+  VecRef wn;
   int next_kind;  // 0 RMSNorm, 1 LayerNorm (no affine)
   float next_eps;
   const int32_t* row_sample;
@@ -103,6 +101,14 @@ struct PostNormArgs {
   float eps;
 };
 hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s);
+
+// fold[b][slot][d] for slot = 4*block + chunk (chunks: attention pre-norm,
+// attention post-norm, FFN pre-norm, FFN post-norm) and the final slot
+// 4*n_blocks:  normw[slot][d] * (1 + s) for chunks 0 and 2, normw[slot][d] *
+// tanh(g) for 1 and 3 (s, g = the block's adaLN output; unmodulated blocks,
+// mod_idx < 0, take normw alone), and 1 + s_final for the final slot.
+hipError_t launch_fold_mod(const float* mod, int64_t mod_stride, const float* normw, const int32_t* mod_idx,
+                           int n_blocks, int n_mod, int D, int B, float* fold, hipStream_t s);
 
 // Caption features (fp32 or bf16 rows of width Dc) -> bf16 RMSNorm(x; w).
 hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t* out,

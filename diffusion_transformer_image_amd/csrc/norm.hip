@@ -22,26 +22,14 @@ constexpr int MAXV = 16;  // float4 per lane: hidden size up to 4096
 
 ZI_DEV float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// modulation value for (sample, d): scale -> 1 + m, gate -> tanh(m)
-ZI_DEV float4 mod_scale(const ModRef& m, int sample, int d) {
-  if (!m.mod) return make_float4(1.f, 1.f, 1.f, 1.f);
-  const float4 v = ld4(m.mod + (int64_t)sample * m.stride + m.off + d);
-  return make_float4(1.f + v.x, 1.f + v.y, 1.f + v.z, 1.f + v.w);
-}
-ZI_DEV float4 mod_gate(const ModRef& m, int sample, int d) {
-  if (!m.mod) return make_float4(1.f, 1.f, 1.f, 1.f);
-  const float4 v = ld4(m.mod + (int64_t)sample * m.stride + m.off + d);
-  return make_float4(tanhf(v.x), tanhf(v.y), tanhf(v.z), tanhf(v.w));
-}
-
 ZI_DEV void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
   u32x2 u = {pack2bf(a, b), pack2bf(c, d)};
   *reinterpret_cast<u32x2*>(p) = u;
 }
 
-// normalise the row held in v[] (nv float4 per lane) and write bf16
-ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float eps,
-                       const float* w, const ModRef& sc, int sample, bf16_t* h) {
+// normalise the row held in v[] (nv float4 per lane), scale by the folded
+// vector w and write bf16
+ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float eps, const float* w, bf16_t* h) {
   float mean = 0.f;
   if (kind == 1) {
     float s = 0.f;
@@ -62,11 +50,9 @@ ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float
   for (int i = 0; i < MAXV; ++i)
     if (i < nv) {
       const int d = (lane + 64 * i) * 4;
-      const float4 s = mod_scale(sc, sample, d);
-      float4 ww = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (kind == 0) ww = ld4(w + d);
-      store_bf16x4(h + d, (v[i].x - mean) * inv * ww.x * s.x, (v[i].y - mean) * inv * ww.y * s.y,
-                   (v[i].z - mean) * inv * ww.z * s.z, (v[i].w - mean) * inv * ww.w * s.w);
+      const float4 ww = ld4(w + d);
+      store_bf16x4(h + d, (v[i].x - mean) * inv * ww.x, (v[i].y - mean) * inv * ww.y, (v[i].z - mean) * inv * ww.z,
+                   (v[i].w - mean) * inv * ww.w);
     }
 }
 
@@ -80,9 +66,11 @@ __global__ __launch_bounds__(256) void pre_norm_kernel(PreNormArgs a) {
 #pragma unroll
   for (int i = 0; i < MAXV; ++i)
     if (i < nv) v[i] = ld4(xr + (lane + 64 * i) * 4);
-  norm_write(v, nv, lane, a.D, a.kind, a.eps, a.w, a.scale, a.row_sample[r], a.h + (int64_t)r * a.D);
+  norm_write(v, nv, lane, a.D, a.kind, a.eps, a.w.v + a.row_sample[r] * a.w.stride, a.h + (int64_t)r * a.D);
 }
 
+// Both input rows (y bf16, x fp32) are requested before any arithmetic, so
+// a wave has its whole row in flight at once.
 __global__ __launch_bounds__(256) void post_norm_kernel(PostNormArgs a) {
   const int lane = threadIdx.x & 63;
   const int r = a.r0 + blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -91,35 +79,62 @@ __global__ __launch_bounds__(256) void post_norm_kernel(PostNormArgs a) {
   const int sample = a.row_sample[r];
   const bf16_t* yr = a.y + (int64_t)r * a.D;
   float* xr = a.x + (int64_t)r * a.D;
-  float4 y[MAXV];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < MAXV; ++i)
-    if (i < nv) {
-      const u32x2 u = *reinterpret_cast<const u32x2*>(yr + (lane + 64 * i) * 4);
-      y[i] = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                         __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-      ss += y[i].x * y[i].x + y[i].y * y[i].y + y[i].z * y[i].z + y[i].w * y[i].w;
-    }
-  const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
+  u32x2 yu[MAXV];
   float4 v[MAXV];
 #pragma unroll
   for (int i = 0; i < MAXV; ++i)
     if (i < nv) {
+      yu[i] = *reinterpret_cast<const u32x2*>(yr + (lane + 64 * i) * 4);
+      v[i] = ld4(xr + (lane + 64 * i) * 4);
+    }
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+    if (i < nv) {
+      const float p = __uint_as_float(yu[i].x << 16), q = __uint_as_float(yu[i].x & 0xffff0000u);
+      const float s = __uint_as_float(yu[i].y << 16), t = __uint_as_float(yu[i].y & 0xffff0000u);
+      ss += p * p + q * q + s * s + t * t;
+    }
+  const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)a.D + a.eps);
+  const float* wg = a.wg.v + sample * a.wg.stride;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i)
+    if (i < nv) {
       const int d = (lane + 64 * i) * 4;
-      const float4 g = mod_gate(a.gate, sample, d);
-      const float4 w = ld4(a.w_post + d);
-      float4 x = ld4(xr + d);
-      x.x += g.x * (y[i].x * inv * w.x);
-      x.y += g.y * (y[i].y * inv * w.y);
-      x.z += g.z * (y[i].z * inv * w.z);
-      x.w += g.w * (y[i].w * inv * w.w);
-      *reinterpret_cast<float4*>(xr + d) = x;
-      v[i] = x;
+      const float4 g = ld4(wg + d);
+      v[i].x += __uint_as_float(yu[i].x << 16) * inv * g.x;
+      v[i].y += __uint_as_float(yu[i].x & 0xffff0000u) * inv * g.y;
+      v[i].z += __uint_as_float(yu[i].y << 16) * inv * g.z;
+      v[i].w += __uint_as_float(yu[i].y & 0xffff0000u) * inv * g.w;
+      *reinterpret_cast<float4*>(xr + d) = v[i];
     }
   if (r >= a.n0 && r < a.n1)
-    norm_write(v, nv, lane, a.D, a.next_kind, a.next_eps, a.w_next, a.scale_next, sample,
-               a.h + (int64_t)r * a.D);
+    norm_write(v, nv, lane, a.D, a.next_kind, a.next_eps, a.wn.v + sample * a.wn.stride, a.h + (int64_t)r * a.D);
+}
+
+__global__ void fold_mod_kernel(const float* __restrict__ mod, int64_t mod_stride, const float* __restrict__ normw,
+                                const int32_t* __restrict__ mod_idx, int n_blocks, int n_mod, int D,
+                                float* __restrict__ fold) {
+  const int slots = 4 * n_blocks + 1;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)slots * D) return;
+  const int b = blockIdx.y;
+  const int slot = (int)(idx / D), d = (int)(idx - (int64_t)slot * D);
+  const float* mb = mod + (int64_t)b * mod_stride;
+  float v;
+  if (slot < 4 * n_blocks) {
+    const int bi = slot >> 2, ch = slot & 3, m = mod_idx[bi];
+    const float w = normw[idx];
+    if (m < 0) {
+      v = w;
+    } else {
+      const float u = mb[(int64_t)(m * 4 + ch) * D + d];
+      v = (ch & 1) ? w * tanhf(u) : w * (1.0f + u);
+    }
+  } else {
+    v = 1.0f + mb[(int64_t)n_mod * 4 * D + d];
+  }
+  fold[(int64_t)b * slots * D + idx] = v;
 }
 
 // caption features: one wave per row, any width that is a multiple of 256
@@ -195,6 +210,14 @@ hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t
     hipLaunchKernelGGL(rows_rmsnorm_kernel<true>, dim3((rows + 3) / 4), dim3(256), 0, s, x, w, out, rows, Dc, eps);
   else
     hipLaunchKernelGGL(rows_rmsnorm_kernel<false>, dim3((rows + 3) / 4), dim3(256), 0, s, x, w, out, rows, Dc, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_mod(const float* mod, int64_t mod_stride, const float* normw, const int32_t* mod_idx,
+                           int n_blocks, int n_mod, int D, int B, float* fold, hipStream_t s) {
+  const int64_t n = (int64_t)(4 * n_blocks + 1) * D;
+  hipLaunchKernelGGL(fold_mod_kernel, dim3((unsigned)((n + 255) / 256), B), dim3(256), 0, s, mod, mod_stride, normw,
+                     mod_idx, n_blocks, n_mod, D, fold);
   return hipGetLastError();
 }
 
