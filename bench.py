@@ -129,9 +129,13 @@ def cpu_baseline(wl, model):
 
 # ---------------------------------------------------------------- traffic from committed counters
 
-def source_digest():
+def source_digest(kernel):
+    """Digest of the sources that define a kernel class (its .hip file and the
+    shared headers): counter figures taken on other sources do not apply."""
+    main = "gemm.hip" if kernel.startswith("gemm") or kernel in ("embed", "final_layer") else \
+        "attention.hip" if kernel == "attention" else "norm.hip"
     h = hashlib.sha256()
-    for f in ("gemm.hip", "attention.hip", "norm.hip", "common.h"):
+    for f in (main, "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -146,7 +150,7 @@ def committed_traffic(kernel, workload):
     txt = open(path).read()
     m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", txt)
-    if not m or not d or d.group(1) != source_digest():
+    if not m or not d or d.group(1) != source_digest(kernel):
         return None
     return float(m.group(1))
 
