@@ -145,11 +145,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const float sl2 = a.scale_log2;
 
-  // Online softmax of one score tile in the log2 domain (raw v_exp_f32:
-  // weights below 2^-126 flush to zero).  The reference max m only moves when
-  // a lane's max exceeds it by the slack, so p <= 2^slack; the O rescale is
-  // branch-free (alpha = 1 when m did not move).
-  auto softmax = [&](f32x16* st) {
+  // Online softmax in the log2 domain (raw v_exp_f32: weights below 2^-126
+  // flush to zero).  The reference max m only moves when a lane's max exceeds
+  // it by the slack, so p <= 2^slack; O and l are rescaled only when some lane
+  // of the wave moved its m (a wave-uniform branch; after the first tile of a
+  // row this is rare), since the rescale is as much vector work as the
+  // exponentials themselves.
+  auto stats = [&](f32x16* st) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -157,8 +159,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[tt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
     const float mnew = mx > m + RESCALE_SLACK ? mx : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+    if (__any(mnew != m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      m = mnew;
+    }
+  };
+  auto expsum = [&](f32x16* st) {
     float rs = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -168,11 +179,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         st[tt][e] = p;
         rs += p;
       }
-    l = fmaf(l, alpha, rs + __shfl_xor(rs, 32, 64));
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    l += rs + __shfl_xor(rs, 32, 64);
   };
   // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
   auto pv = [&](const bf16_t* vb, const f32x16* st) {
@@ -189,37 +196,39 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     }
   };
   // the issue order of one pipelined half: scores of the next tile interleaved
-  // with the softmax of the current one, then the PV product
+  // with the exponentials of the current one, then the PV product
   auto pin_order = [&]() {
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0); // VALU (softmax)
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU (exponentials)
     }
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (V operand)
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
     }
   };
 
   // Pipeline: in the half that handles tile t, the scores of tile t+1 are
-  // computed while tile t is normalised and multiplied into O.  K(t+2) and
+  // computed while tile t is exponentiated and multiplied into O.  K(t+2) and
   // V(t+1) are loaded meanwhile into the buffers freed by the previous half.
-  // A half contains no branches (the mask is always applied), so the
-  // scheduler can interleave matrix and vector work.
-  auto half = [&](const bf16_t* kn, const bf16_t* vc, f32x16* scur, f32x16* snext, int nv_next) {
+  // Masking (partial tiles only) and the rescale are wave-uniform branches
+  // before the pinned matrix/vector interleave.
+  auto half = [&](const bf16_t* kn, const bf16_t* vc, f32x16* scur, f32x16* snext, int nv_cur) {
+    if (nv_cur < KTILE) mask(scur, nv_cur);
+    stats(scur);
     qk(kn, snext);
-    mask(snext, nv_next);
-    softmax(scur);
+    expsum(scur);
     pv(vc, scur);
     pin_order();
   };
 
-  // The tile count is padded to an even number (>= 2) with empty tiles: no
-  // loads, every score masked, so their weights are exactly zero.  The loop
+  // The tile count is padded to an even number (>= 2) with an empty tile: its
+  // K is not loaded and every score is masked (selected to -inf), so its
+  // weights are exactly zero, and its V is a copy of a real tile.  The loop
   // body is then the same for every pair of tiles, with no tail.  Indexes j
   // are relative to the unit's first tile tb.
   const int Tp = tn + (tn & 1);
@@ -230,18 +239,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   dma_barrier();
   f32x16 sc[2], sn[2];
   qk(K0, sc);
-  mask(sc, nvalid(0));
   for (int j = 0; j < Tp; j += 2) {
     dma_barrier();  // K(j+1), V(j) landed; everyone is done with K(j) and V(j-1)
     if (j + 2 < tn) dma_k(tb + j + 2, K0);
-    if (j + 1 < tn) dma_v(tb + j + 1, V1);
-    const int nv1 = nvalid(j + 1);
-    half(K1, V0, sc, sn, nv1);
+    // V of tile j+1; for the padding tile (j + 1 == tn) the last real tile, so
+    // that its zero weights multiply finite values
+    dma_v(tb + min(j + 1, tn - 1), V1);
+    half(K1, V0, sc, sn, nvalid(j));
     dma_barrier();
     if (j + 3 < tn) dma_k(tb + j + 3, K1);
     if (j + 2 < tn) dma_v(tb + j + 2, V0);
-    const int nv2 = nvalid(j + 2);  // past the end: a throwaway, fully masked tile
-    half(K0, V1, sn, sc, nv2);
+    half(K0, V1, sn, sc, nvalid(j + 1));  // j + 1 == tn: the padding tile, fully masked
   }
 
   if (qi < it.nq && unit >= 0) {
