@@ -95,24 +95,36 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // K: chunk p -> LDS row R = p/16 (holds key 32*(R/32) + swap_bits23(R%32)),
   //    stored position p%16 holds logical chunk (p%16) ^ (R & 15).
   // V^T: chunk p -> row d = p/8, stored position p%8 holds keys 8*((p%8) ^ ((d>>1)&7)).
+  // With p = (4 i + wave) * 64 + lane these reduce to: K load i fetches key
+  // 16 i + kk0 at chunk hc, V^T load i fetches row 32 i + dd0 at key chunk kc,
+  // where kk0, hc, dd0, kc depend on the lane only -- so each lane keeps one
+  // 32-bit offset per operand and the per-tile address work is scalar.
+  const int r0 = wave * 4 + (lane >> 4);
+  const int kk0 = swap_bits23(r0), hc = (lane & 15) ^ r0;
+  const uint32_t koff0 = (uint32_t)(kk0 * (int)ld + hc * 8);
+  const int dd0 = wave * 8 + (lane >> 3);
+  const uint32_t voff0 = (uint32_t)(dd0 * a.S_pad + (((lane & 7) ^ ((dd0 >> 1) & 7)) << 3));
   auto dma_k = [&](int t, bf16_t* kb) {
     const int kr0 = tile_start(t), nv = tile_valid(t);
+    const bf16_t* base = a.qkv + (int64_t)kr0 * ld + D + h * HD;
+    if (nv == KTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane, R = p >> 4, hc = (p & 15) ^ (R & 15);
-      const int key = (R & 32) | swap_bits23(R & 31);
-      const bf16_t* src = a.qkv + (int64_t)(kr0 + min(key, nv - 1)) * ld + D + h * HD + hc * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)i * 16 * ld + koff0),
+                                         LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
+    } else {  // last tile of a range: keys past its end are clamped
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)min(16 * i + kk0, nv - 1) * ld + hc * 8),
+                                         LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
     }
   };
   auto dma_v = [&](int t, bf16_t* vb) {
-    const int kr0 = tile_start(t);
+    const bf16_t* base = a.vT + (int64_t)(h * HD) * a.S_pad + tile_start(t);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane, d = p >> 3, kc = (p & 7) ^ ((d >> 1) & 7);
-      const bf16_t* src = a.vT + (int64_t)(h * HD + d) * a.S_pad + kr0 + kc * 8;
-      __builtin_amdgcn_global_load_lds((const void*)src, LDS_PTR(vb + (i * 4 + wave) * 512), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)i * 32 * a.S_pad + voff0),
+                                       LDS_PTR(vb + (i * 4 + wave) * 512), 16, 0, 0);
   };
   // S^T for 64 keys x this wave's 32 queries; with MASK, keys past nv -> -inf
   auto qk = [&](const bf16_t* kb, f32x16* st) {
