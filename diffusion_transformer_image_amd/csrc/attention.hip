@@ -34,6 +34,7 @@ constexpr int HD = 128;  // head_dim
 constexpr int KTILE = 64;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units: stale row max may lag by 2^8
 constexpr int MAX_SPLIT = 16;          // key-tile chunks per split (item, head) pair
+constexpr int AHEAD = 3;               // LDS operand reads issued ahead of their MFMA
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -127,16 +128,23 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
                                        LDS_PTR(vb + (i * 4 + wave) * 512), 16, 0, 0);
   };
   // S^T for 64 keys x this wave's 32 queries; with MASK, keys past nv -> -inf
+  // Operand reads run AHEAD reads ahead of the MFMA that consumes them
+  // (a small ring of fragments), so an MFMA never waits on the LDS read issued
+  // just before it.
   auto qk = [&](const bf16_t* kb, f32x16* st) {
     st[0] = f32x16{};
     st[1] = f32x16{};
+    auto kread = [&](int i) {  // i = 2 ks + tt
+      return *reinterpret_cast<const bf16x8*>(kb + ((i & 1) * 32 + lrow) * HD + (((2 * (i >> 1) + lhalf) ^ swk) << 3));
+    };
+    bf16x8 kf[AHEAD + 1];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int i = 0; i < AHEAD; ++i) kf[i] = kread(i);
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + (tt * 32 + lrow) * HD + (((2 * ks + lhalf) ^ swk) << 3));
-        st[tt] = mfma32(kf, qf[ks], st[tt]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + AHEAD < 16) kf[(i + AHEAD) % (AHEAD + 1)] = kread(i + AHEAD);
+      st[i & 1] = mfma32(kf[i % (AHEAD + 1)], qf[i >> 1], st[i & 1]);
+    }
   };
   auto mask = [&](f32x16* st, int nv) {
     // key of element e is c_e + 8*lhalf with c_e a compile-time constant;
@@ -195,30 +203,37 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   };
   // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
   auto pv = [&](const bf16_t* vb, const f32x16* st) {
+    auto vread = [&](int i) {  // i = 4 s + dt
+      return *reinterpret_cast<const bf16x8*>(vb + ((i & 3) * 32 + lrow) * KTILE + (((2 * (i >> 2) + lhalf) ^ swv) << 3));
+    };
+    bf16x8 vf[AHEAD + 1];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 pf;
+    for (int i = 0; i < AHEAD; ++i) vf[i] = vread(i);
+    bf16x8 pf;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pf[u] = (__bf16)st[s >> 1][(s & 1) * 8 + u];
+    for (int i = 0; i < 16; ++i) {
+      if (i + AHEAD < 16) vf[(i + AHEAD) % (AHEAD + 1)] = vread(i + AHEAD);
+      if ((i & 3) == 0) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vb + (dt * 32 + lrow) * KTILE + (((2 * s + lhalf) ^ swv) << 3));
-        o[dt] = mfma32(vf, pf, o[dt]);
+        for (int u = 0; u < 8; ++u) pf[u] = (__bf16)st[i >> 3][((i >> 2) & 1) * 8 + u];
       }
+      o[i & 3] = mfma32(vf[i % (AHEAD + 1)], pf, o[i & 3]);
     }
   };
   // the issue order of one pipelined half: scores of the next tile interleaved
   // with the exponentials of the current one, then the PV product
   auto pin_order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first K operand reads
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
+      if (g + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU (exponentials)
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first V operand reads
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (V operand)
+      if (g + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (V operand)
       __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
     }
