@@ -216,6 +216,55 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
   }
 }
 
+// bf16 epilogues of full-width 256x256 tiles (plain, and SwiGLU with its
+// 256x128 output) go through LDS so that global stores are 16-byte runs of
+// whole rows instead of 2-byte stores from the accumulator layout.  The four
+// 32 KB operand buffers hold the output tile, row r in buffer r / RPB; the
+// 16-byte chunk k of a row is stored at position k ^ (r & 15), so neither
+// the accumulator-order writes nor the row-order reads conflict.
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void staged_bf16_epilogue(const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0,
+                                                     int M, const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2,
+                                                     bf16_t* s3) {
+  static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "staged epilogue tiling");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_SWIGLU, "bf16 outputs only");
+  constexpr int TM = 4, TN = 2;
+  constexpr int OW = EPI == EPI_SWIGLU ? BN / 2 : BN;  // output columns of the tile
+  constexpr int CPR = OW / 8;                           // 16-byte chunks per output row
+  constexpr int RPB = 16384 / OW;                       // rows per 32 KB buffer
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  auto region = [&](int k) { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
+  __syncthreads();  // every wave has finished reading the operand buffers
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int rb = wm * 128 + i * 32;  // 32 rows, all in one buffer
+    bf16_t* rg = region(rb / RPB);
+#pragma unroll
+    for (int j = 0; j < TN; j += (EPI == EPI_SWIGLU ? 2 : 1)) {
+      const int c = EPI == EPI_SWIGLU ? wn * 32 + lrow : wn * 64 + j * 32 + lrow;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = rb + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+        float v = acc[i][j][e];
+        if constexpr (EPI == EPI_SWIGLU) v = v / (1.0f + __expf(-v)) * acc[i][j + 1][e];
+        rg[(r % RPB) * OW + (((c >> 3) ^ (r & 15)) << 3) + (c & 7)] = f2bf(v);
+      }
+    }
+  }
+  __syncthreads();
+  bf16_t* C = reinterpret_cast<bf16_t*>(ep.C);
+  const int c0 = EPI == EPI_SWIGLU ? n0 / 2 : n0;
+#pragma unroll
+  for (int it = 0; it < BM * CPR / 512; ++it) {
+    const int q = it * 512 + tid, r = q / CPR, k = q % CPR;
+    if (m0 + r >= M) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region(r / RPB) + (r % RPB) * OW + ((k ^ (r & 15)) << 3));
+    *reinterpret_cast<u32x4*>(C + (int64_t)(m0 + r) * ep.ldc + c0 + k * 8) = v;
+  }
+}
+
 // ROLE only separates the symbols of the projections (qkv, out, w1|w3, w2,
 // embeds, final) so that profiles attribute time per projection.
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
@@ -364,6 +413,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   }
   if constexpr (EPI == EPI_QKV_ROPE)
     qkv_rope_epilogue<BM, BN, WM, WN>(acc, m0, n0, M, ep, As0, Bs0, As1, Bs1);
+  else if constexpr ((EPI == EPI_BF16 || EPI == EPI_SWIGLU) && BM == 256 && BN == 256)
+    staged_bf16_epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, ep, As0, Bs0, As1, Bs1);
   else
     epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
 }
@@ -582,6 +633,8 @@ const char* gemm_check(const GemmArgs& g) {
   if (g.epi == EPI_SWIGLU && g.N % 256) return "gemm: SwiGLU needs N a multiple of 256";
   if (g.lda < g.K || g.ldw < g.K) return "gemm: leading dimension smaller than K";
   if ((g.lda % 8) || (g.ldw % 8)) return "gemm: lda and ldw must be multiples of 8";
+  if ((g.epi == EPI_BF16 || g.epi == EPI_SWIGLU) && ((g.ep.ldc % 8) || ((uintptr_t)g.ep.C & 15)))
+    return "gemm: bf16 output needs ldc a multiple of 8 and a 16-byte aligned C";
   if (!g.A || !g.W || !g.ep.C) return "gemm: null pointer";
   if (g.epi == EPI_UNPATCH && (g.ep.ntok <= 0 || g.ep.npad < g.ep.ntok || g.ep.Wp <= 0 || g.ep.C_ch <= 0 || g.ep.patch <= 0))
     return "gemm: bad unpatchify geometry";

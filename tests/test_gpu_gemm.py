@@ -84,6 +84,29 @@ def test_gemm_swiglu(M, F, K):
     assert helpers.rel_l2(got, ref) <= 5e-3
 
 
+@pytest.mark.parametrize("epi", ["bf16", "swiglu"])
+def test_gemm_strided_output_leaves_other_columns(epi):
+    """Row stride ldc > output width, ragged M: only the output columns of the
+    M rows change (bf16 tiles are written as whole-row 16-byte runs)."""
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    M, N, K = 300, 512, 256
+    A, W = _operands(M, N, K, 11)
+    width = N // 2 if epi == "swiglu" else N
+    buf = torch.full((M + 8, width + 72), float("nan"), dtype=torch.bfloat16, device="cuda")
+    C = buf[:M, :width]
+    binding.gemm_bf16(_dev_bf16(A), _dev_bf16(W), C, binding.EPI_SWIGLU if epi == "swiglu" else binding.EPI_BF16)
+    torch.cuda.synchronize()
+    out = buf.float().cpu().numpy()
+    assert np.isnan(out[:, width:]).all() and np.isnan(out[M:]).all()
+    got = out[:M, :width]
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    if epi == "swiglu":  # rows of W interleaved in groups of 32: (w1 block, w3 block)
+        idx = np.arange(N).reshape(-1, 64)
+        ref = om.silu(ref[:, idx[:, :32].ravel()]) * ref[:, idx[:, 32:].ravel()]
+    assert helpers.rel_l2(got, ref) <= 5e-3
+
+
 def test_gemm_rejects_bad_shapes():
     torch = _torch()
     from diffusion_transformer_image_amd import binding
@@ -93,3 +116,9 @@ def test_gemm_rejects_bad_shapes():
     with pytest.raises(binding.ZimgError) as ei:
         binding.gemm_bf16(A, W, C)
     assert ei.value.code == binding.ZIMG_EINVAL and "multiple of 64" in str(ei.value)
+    A = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    Cw = torch.zeros((16, 70), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(binding.ZimgError) as ei:
+        binding.gemm_bf16(A, W, Cw[:, :64])
+    assert ei.value.code == binding.ZIMG_EINVAL and "ldc" in str(ei.value)
