@@ -10,6 +10,12 @@ the output is negated to match the noise - latents flow target; the fixed
 shift is 3.0.  [FV] "Pinned official pipeline context" / "Scheduler": the
 schedule has num_steps + 1 points ending at sigma = 0, and no DiT call is
 made at that final zero point.
+
+Classifier-free guidance: [FV] "Pinned official pipeline context" lists a
+negative prompt, ``guidance_scale`` (default 0.0) and ``cfg_truncation``
+(default 1.0); [AIT] "Specifics" says the UI's guidance scale reaches the
+pipeline reduced by one; the base model runs 28-50 steps at CFG 3-5 ("Z-Image"
+model card, native output).
 """
 
 import numpy as np
@@ -57,6 +63,46 @@ def run(model_fn, latent0, n_steps=8, shift=3.0, on_step=None):
     for k in range(n_steps):
         tk = np.full(B, np.float32(t[k]), dtype=np.float64)
         out = model_fn(x, tk)
+        x = euler_step(x, out, sig[k], sig[k + 1])
+        if on_step is not None:
+            on_step(k, x, out)
+    return x
+
+
+def guided_output(out_cond, out_uncond, guidance):
+    """Classifier-free guidance as the pipeline receives it.  The pipeline's
+    guidance scale g is the user-facing scale minus one ([AIT] "Specifics":
+    a UI scale of 4 reaches the pipeline as 3), so the guided prediction is
+    the conditional output pushed away from the unconditional one by g times
+    their difference; g = 0 (the Turbo default, [FV] "Pinned official
+    pipeline context" / "Official defaults") is the conditional output."""
+    c = np.asarray(out_cond, np.float64)
+    u = np.asarray(out_uncond, np.float64)
+    return c + guidance * (c - u)
+
+
+def guidance_active(t, cfg_truncation):
+    """Reading of ``cfg_truncation`` (the pages give only its default, 1.0):
+    guidance is applied at steps whose model time t (0 = noise, 1 = clean)
+    is at most cfg_truncation, so 1.0 keeps it on every step and smaller
+    values switch it off for the last, nearly clean steps.  Both values are
+    compared as float32, as the engine's sampler does."""
+    return bool(np.float32(t) <= np.float32(cfg_truncation))
+
+
+def run_cfg(model_fn, latent0, n_steps=28, shift=3.0, guidance=3.0, cfg_truncation=1.0, on_step=None):
+    """Euler loop with classifier-free guidance.  ``model_fn(x, t_vector,
+    cond)`` is the oracle forward with the conditional (cond=True) or the
+    unconditional (negative) caption.  A step where guidance is off (g = 0 or
+    truncated) calls only the conditional forward."""
+    sig, t = schedule(n_steps, shift)
+    x = np.asarray(latent0, dtype=np.float64)
+    B = x.shape[0]
+    for k in range(n_steps):
+        tk = np.full(B, np.float32(t[k]), dtype=np.float64)
+        out = model_fn(x, tk, True)
+        if guidance != 0.0 and guidance_active(t[k], cfg_truncation):
+            out = guided_output(out, model_fn(x, tk, False), guidance)
         x = euler_step(x, out, sig[k], sig[k + 1])
         if on_step is not None:
             on_step(k, x, out)

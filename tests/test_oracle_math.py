@@ -393,3 +393,56 @@ def test_sampler_endpoints_and_euler_sign():
         # the model's raw output is the negated flow target (output negated before the step)
         x = osm.euler_step(x, -(noise - x0), sig[k], sig[k + 1])
     np.testing.assert_allclose(x, x0, rtol=1e-12, atol=1e-12)
+
+
+def test_cfg_guidance_algebra():
+    """The pipeline's scale g is the UI scale minus one: c + g (c - u) equals
+    the textbook u + s (c - u) with s = g + 1; g = 0 and c = u give c."""
+    rng = np.random.default_rng(3)
+    c, u = rng.standard_normal((2, 5, 7))
+    for s_ui in (1.0, 4.0, 5.0):
+        np.testing.assert_allclose(osm.guided_output(c, u, s_ui - 1.0), u + s_ui * (c - u), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(osm.guided_output(c, u, 0.0), c)
+    assert np.array_equal(osm.guided_output(c, c, 3.0), c)
+
+
+def test_cfg_loop_reduces_to_plain_loop_and_closed_form():
+    rng = np.random.default_rng(4)
+    x0 = rng.standard_normal((1, 3))
+    a, b = rng.standard_normal((2, 1, 3))
+    calls = []
+
+    def model(x, t, cond):  # raw output x - target: a velocity field pulling towards the target
+        calls.append(cond)
+        return x - (a if cond else b)
+
+    # g = 0: the conditional forward only, identical to the plain loop
+    plain = osm.run(lambda x, t: model(x, t, True), x0, n_steps=6, shift=3.0)
+    calls.clear()
+    np.testing.assert_array_equal(osm.run_cfg(model, x0, n_steps=6, shift=3.0, guidance=0.0), plain)
+    assert calls == [True] * 6
+    # guided output x - a', a' = a + g (a - b); Euler: x_{k+1} - a' = (x_k - a') (1 + sig_k - sig_{k+1})
+    g = 2.5
+    ap = a + g * (a - b)
+    sig, _ = osm.schedule(6, 3.0)
+    want = ap + (x0 - ap) * np.prod(1.0 + sig[:-1] - sig[1:])
+    calls.clear()
+    got = osm.run_cfg(model, x0, n_steps=6, shift=3.0, guidance=g)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    assert calls.count(False) == 6
+
+
+def test_cfg_truncation_switches_guidance_off_late():
+    _, t = osm.schedule(8, 3.0)
+    assert all(osm.guidance_active(tk, 1.0) for tk in t)  # default: every step
+    on = [osm.guidance_active(tk, 0.5) for tk in t]
+    assert on == [tk <= 0.5 for tk in t] and any(on) and not all(on)
+    assert on == sorted(on, reverse=True)  # a prefix of the steps (t grows towards clean)
+    calls = []
+
+    def model(x, tt, cond):
+        calls.append(cond)
+        return 0.1 * x
+
+    osm.run_cfg(model, np.ones((1, 2)), n_steps=8, shift=3.0, guidance=3.0, cfg_truncation=0.5)
+    assert calls.count(False) == sum(on) and calls.count(True) == 8
