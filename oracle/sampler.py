@@ -14,8 +14,8 @@ made at that final zero point.
 Classifier-free guidance: [FV] "Pinned official pipeline context" lists a
 negative prompt, ``guidance_scale`` (default 0.0) and ``cfg_truncation``
 (default 1.0); [AIT] "Specifics" says the UI's guidance scale reaches the
-pipeline reduced by one; the base model runs 28-50 steps at CFG 3-5 ("Z-Image"
-model card, native output).
+pipeline reduced by one; the base model runs 28-50 steps at CFG 3-5 ([AIT],
+the model summary above "Components").
 """
 
 import numpy as np
