@@ -93,6 +93,7 @@ SIGNATURES = {
     "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
     "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
+    "zimg_cfg_euler_step": (_I32, [_P, _P, _P, ctypes.c_float, ctypes.c_float, _I64, _P]),
     "zimg_dit_profile": (_I32, [_P, _I32]),
     "zimg_dit_profile_read": (_I32, [_P, ctypes.POINTER(KernelStat), _I32, _I32P]),
     "zimg_dit_attention_plan": (_I32, [_P, _I32, _I32P]),
@@ -303,6 +304,13 @@ def gemm_bf16(A, W, C, epilogue=EPI_BF16, bias=None, stream=None):
     _check(lib().zimg_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), _ptr(C), C.stride(0), M, N, K,
                                 epilogue, _ptr(bias) if bias is not None else None, _stream(stream)))
     return C
+
+
+def cfg_euler_step(x, out_cond, out_uncond, guidance, dt, stream=None):
+    """x += dt * -(out_cond + guidance * (out_cond - out_uncond)) (torch CUDA fp32)."""
+    _check(lib().zimg_cfg_euler_step(_ptr(x), _ptr(out_cond), _ptr(out_uncond), float(guidance), float(dt),
+                                     x.numel(), _stream(stream)))
+    return x
 
 
 def euler_step(x, model_out, dt, stream=None):

@@ -1220,6 +1220,17 @@ int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stat
   return ZIMG_OK;
 }
 
+int zimg_cfg_euler_step(float* x, const float* out_cond, const float* out_uncond, float guidance, float dt,
+                        int64_t n, void* stream) {
+  g_last_error.clear();
+  if (n < 0) return set_err(ZIMG_EINVAL, "n is negative");
+  if (n > 0 && (!x || !out_cond || !out_uncond)) return set_err(ZIMG_EINVAL, "NULL buffer");
+  if (!std::isfinite(dt) || !std::isfinite(guidance)) return set_err(ZIMG_EINVAL, "dt or guidance is not finite");
+  if (n > 0 && (x == out_cond || x == out_uncond)) return set_err(ZIMG_EINVAL, "x aliases a model output");
+  HIP_TRY(zimg::launch_cfg_euler(x, out_cond, out_uncond, guidance, dt, n, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
 int zimg_dit_attention_plan(zimg_dit* h, int32_t stage, int32_t out[3]) {
   g_last_error.clear();
   if (!h || !out) return set_err(ZIMG_EINVAL, "NULL argument");

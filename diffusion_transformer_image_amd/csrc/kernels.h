@@ -161,6 +161,9 @@ hipError_t launch_gemv(const bf16_t* W, const float* bias, const float* x, int64
                        float* y, int64_t ldy, int N, int K, int B, int act, hipStream_t s);
 // x[i] += dt * (-o[i])
 hipError_t launch_euler(float* x, const float* o, float dt, int64_t n, hipStream_t s);
+// x += dt * -(oc + g (oc - ou)), n elements
+hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g, float dt, int64_t n,
+                            hipStream_t s);
 // fill n floats with v
 hipError_t launch_fill(float* p, float v, int64_t n, hipStream_t s);
 

@@ -81,6 +81,25 @@ __global__ void euler_kernel(float* x, const float* o, float dt, int64_t n) {
   if (i < n) x[i] = fmaf(dt, -o[i], x[i]);
 }
 
+// Guided Euler update: the guided prediction c + g (c - u) and the step
+// x += dt * (-prediction) in one pass (16 B of HBM traffic per element).
+// Four elements per thread when every pointer is 16-byte aligned.
+__global__ void cfg_euler4_kernel(float4* x, const float4* oc, const float4* ou, float g, float dt, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 c = oc[i], u = ou[i];
+  float4 v = x[i];
+  v.x = fmaf(dt, -fmaf(g, c.x - u.x, c.x), v.x);
+  v.y = fmaf(dt, -fmaf(g, c.y - u.y, c.y), v.y);
+  v.z = fmaf(dt, -fmaf(g, c.z - u.z, c.z), v.z);
+  v.w = fmaf(dt, -fmaf(g, c.w - u.w, c.w), v.w);
+  x[i] = v;
+}
+__global__ void cfg_euler_kernel(float* x, const float* oc, const float* ou, float g, float dt, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = fmaf(dt, -fmaf(g, oc[i] - ou[i], oc[i]), x[i]);
+}
+
 __global__ void fill_kernel(float* p, float v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -110,6 +129,18 @@ hipError_t launch_gemv(const bf16_t* W, const float* bias, const float* x, int64
 
 hipError_t launch_euler(float* x, const float* o, float dt, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(euler_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, o, dt, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g, float dt, int64_t n,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const bool vec = n % 4 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)oc & 15) == 0 && ((uintptr_t)ou & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(cfg_euler4_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, (float4*)x,
+                       (const float4*)oc, (const float4*)ou, g, dt, n / 4);
+  else
+    hipLaunchKernelGGL(cfg_euler_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, oc, ou, g, dt, n);
   return hipGetLastError();
 }
 

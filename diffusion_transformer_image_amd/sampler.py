@@ -42,3 +42,44 @@ def euler_loop(dit, latent, caption_feats, caption_lens, n_steps=8, shift=3.0, o
             on_step(k, latent, out)
         binding.euler_step(latent, out, float(sig[k + 1] - sig[k]), stream=stream)
     return latent
+
+
+def guidance_active(t, cfg_truncation):
+    """Guidance is applied at model times t <= cfg_truncation (compared in
+    float32); the default 1.0 applies it on every step."""
+    return bool(np.float32(t) <= np.float32(cfg_truncation))
+
+
+def cfg_euler_loop(dit, latent, caps_cond, lens_cond, caps_uncond, lens_uncond, n_steps=28, shift=3.0,
+                   guidance=3.0, cfg_truncation=1.0, on_step=None):
+    """Euler loop with classifier-free guidance, in place on ``latent``
+    (torch CUDA fp32 [B, C, Hl, Wl]).  Each guided step runs one forward of
+    the batch [latent; latent] with captions [cond; uncond] (``caps_*``:
+    packed CUDA rows, ``lens_*``: B lengths each) and one fused update
+    (zimg_cfg_euler_step); a step without guidance (guidance 0 or model time
+    past ``cfg_truncation``) runs the conditional half alone.  The engine
+    needs max_batch >= 2 B.  ``guidance`` is the pipeline's scale (the
+    user-facing scale minus one).  Everything runs on torch's current
+    stream.  Returns ``latent``."""
+    import torch
+    sig, t = schedule(n_steps, shift)
+    B = latent.shape[0]
+    pair = torch.empty((2 * B,) + tuple(latent.shape[1:]), dtype=latent.dtype, device=latent.device)
+    out = torch.empty_like(pair)
+    caps_pair = torch.cat([caps_cond, caps_uncond])
+    lens_pair = list(lens_cond) + list(lens_uncond)
+    for k in range(n_steps):
+        dt = float(sig[k + 1] - sig[k])
+        if guidance != 0.0 and guidance_active(t[k], cfg_truncation):
+            pair[:B].copy_(latent)
+            pair[B:].copy_(latent)
+            dit.forward(pair, caps_pair, lens_pair, np.full(2 * B, t[k], dtype=np.float32), out)
+            if on_step is not None:
+                on_step(k, latent, out)
+            binding.cfg_euler_step(latent, out[:B], out[B:], guidance, dt)
+        else:
+            dit.forward(latent, caps_cond, list(lens_cond), np.full(B, t[k], dtype=np.float32), out[:B])
+            if on_step is not None:
+                on_step(k, latent, out[:B])
+            binding.euler_step(latent, out[:B], dt)
+    return latent

@@ -67,6 +67,20 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
 int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void* stream);
 
 /*
+ * Guided Euler update with classifier-free guidance, one fused pass:
+ * x[i] += dt * -(out_cond[i] + guidance * (out_cond[i] - out_uncond[i])).
+ * ``guidance`` is the pipeline's scale, i.e. the user-facing scale minus
+ * one ("Z-Image" (AI Toolkit docs), Specifics), so 0 is the unguided step;
+ * the negated output and dt as for zimg_euler_step ("Local component
+ * coverage and quality handoff for the zimage FastVideo port", Pinned
+ * official pipeline context: negative prompt, guidance_scale).  x, out_cond,
+ * out_uncond DEVICE fp32 [n]; x may not alias the outputs.  ZIMG_EINVAL for
+ * NULL pointers (n > 0), n < 0, or a non-finite dt or guidance.
+ */
+int zimg_cfg_euler_step(float* x, const float* out_cond, const float* out_uncond, float guidance, float dt,
+                        int64_t n, void* stream);
+
+/*
  * Per-kernel timing of forwards on a handle, for measurement: while
  * enabled, every kernel (or small group of launches) of a forward is
  * bracketed by HIP events recorded on the forward's stream, and the elapsed
