@@ -131,11 +131,12 @@ def cpu_baseline(wl, model):
 
 def source_digest(kernel):
     """Digest of the sources that define a kernel class (its .hip file and the
-    shared headers): counter figures taken on other sources do not apply."""
+    shared device header): counter figures taken on other sources do not
+    apply."""
     main = "gemm.hip" if kernel.startswith("gemm") or kernel in ("embed", "final_layer") else \
         "attention.hip" if kernel == "attention" else "norm.hip"
     h = hashlib.sha256()
-    for f in (main, "common.h", "kernels.h"):
+    for f in (main, "common.h"):
         with open(os.path.join(ROOT, "diffusion_transformer_image_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -155,6 +156,56 @@ def committed_traffic(kernel, workload):
     return float(m.group(1))
 
 
+# ---------------------------------------------------------------- guided step
+
+def guided_step(dit, wl, lat, caps, lens, n_img, stream, steps=3, neg_len=32, guidance=3.0, dt=-0.05):
+    """One classifier-free-guided sampler step at the same geometry: the
+    forward of [latent; latent] with [caption; 32-token negative caption] and
+    the fused guided Euler update; plus the update kernel alone."""
+    import numpy as np
+    import torch
+    import synthetic
+    from diffusion_transformer_image_amd import binding
+    B = lat.shape[0]
+    neg = torch.from_numpy(np.concatenate(synthetic.captions([neg_len] * B, seed=wl["seed"] + 1))).cuda()
+    caps_pair = torch.cat([caps, neg])
+    lens_pair = list(lens) + [neg_len] * B
+    pair = torch.empty((2 * B,) + tuple(lat.shape[1:]), device="cuda")
+    pout = torch.empty_like(pair)
+    x = lat.clone()
+    tt = [0.5] * (2 * B)
+
+    def step():
+        pair[:B].copy_(x)
+        pair[B:].copy_(x)
+        dit.forward(pair, caps_pair, lens_pair, tt, pout)
+        binding.cfg_euler_step(x, pout[:B], pout[B:], guidance, dt)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    reps = 50
+    e0.record(stream)
+    for _ in range(reps):
+        binding.cfg_euler_step(x, pout[:B], pout[B:], guidance, dt)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    upd_us = e0.elapsed_time(e1) / reps * 1e3
+    n = x.numel()
+    tokens = 2 * B * n_img + sum(lens) + B * neg_len
+    return {"workload": f"guided step at the same geometry: forward of [latent; latent] with "
+                        f"[caption; {neg_len}-token negative caption] + fused guided Euler update",
+            "ms_per_step": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "update_us": round(upd_us, 2), "update_GBps": round(16.0 * n / (upd_us * 1e-6) / 1e9, 1),
+            "update_bytes_per_element": 16}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -164,6 +215,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dit_1024")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cfg-steps", type=int, default=3, metavar="K",
+                    help="also time K classifier-free-guided steps (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also launch one plain device copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -193,7 +246,8 @@ def main():
     tokens = B * n_img + sum(lens)
     t = list(wl["t"]) if wl.get("t") else [0.5] * B
 
-    cfg = binding.config(max_batch=B, max_image_tokens=n_img, max_caption_tokens=max(lens), **model)
+    # workspace for 2 B samples: the guided step runs [latent; latent]
+    cfg = binding.config(max_batch=2 * B, max_image_tokens=n_img, max_caption_tokens=max(lens), **model)
     W = synthetic.SyntheticWeights(binding.manifest(cfg), seed=wl["seed"], outlier_log2=wl.get("outlier_log2"))
     t0 = time.perf_counter()
     log(f"drawing and uploading {len(W)} weight tensors ({args.workload})")
@@ -230,6 +284,10 @@ def main():
     torch.cuda.synchronize()
     stats = dit.profile_read()
     dit.profile(False)
+
+    cfg_step = guided_step(dit, wl, lat, caps, lens, n_img, stream) if args.cfg_steps > 0 else None
+    if cfg_step is not None:
+        log(f"guided step: {cfg_step['ms_per_step']:.2f} ms")
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -293,6 +351,8 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    if cfg_step is not None:
+        result["cfg_step"] = cfg_step
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, model) if B == 1 else None
