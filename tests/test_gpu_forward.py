@@ -123,6 +123,20 @@ def test_forward_small_varlen_batch():
     print(rep)
 
 
+@pytest.mark.parametrize("latent,lens", [
+    ((1, 16, 2, 2), (1,)),                # one image token, one caption token
+    ((3, 16, 4, 6), (1, 77, 33)),         # 6 image tokens; captions of 1, 77 and 33 tokens
+    ((2, 16, 2, 34), (64, 65)),           # 1 x 17 image tokens; captions at a tile edge and one past it
+])
+def test_forward_degenerate_geometries(latent, lens):
+    """Smallest images and captions, single-tile and one-past-a-tile key
+    ranges, batches mixing them: every block against the oracle."""
+    n_img = (latent[2] // 2) * (latent[3] // 2)
+    t = tuple(0.2 + 0.3 * i for i in range(len(lens)))
+    rep, _ = _compare_forward(SMALL, latent, lens, t, n_img, max(lens))
+    print(rep[-1])
+
+
 @pytest.mark.parametrize("batch_invariant", [0, 1])
 def test_determinism_and_batch_independence(batch_invariant):
     """Two identical calls are bitwise equal.  A sample run alone matches its
