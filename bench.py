@@ -285,7 +285,7 @@ def main():
     stats = dit.profile_read()
     dit.profile(False)
 
-    cfg_step = guided_step(dit, wl, lat, caps, lens, n_img, stream) if args.cfg_steps > 0 else None
+    cfg_step = guided_step(dit, wl, lat, caps, lens, n_img, stream, steps=args.cfg_steps) if args.cfg_steps > 0 else None
     if cfg_step is not None:
         log(f"guided step: {cfg_step['ms_per_step']:.2f} ms")
 
