@@ -17,6 +17,7 @@ import numpy as np
 
 from .config import ModelConfig
 from .manifest import block_prefixes
+from . import quant as qz
 
 
 def _f64(a):
@@ -225,15 +226,28 @@ def attention(q, k, v, q_chunk=2048):
     return out
 
 
-def swiglu_ffn(W, prefix, h):
+def linear(x, w, quant=None, held="f32"):
+    """x W^T without bias.  quant None: float64.  quant "int8": the W8A8
+    product of oracle.quant, with x quantized from the precision it is held
+    in when it reaches the projection (``held``: "f32" or "bf16")."""
+    if quant is None:
+        return _f64(x) @ _f64(w).T
+    if quant != "int8":
+        raise ValueError(f"unknown quantization {quant!r}")
+    xh = qz.to_bf16(x) if held == "bf16" else qz.to_f32(x)
+    return qz.int8_linear(xh, w)
+
+
+def swiglu_ffn(W, prefix, h, quant=None):
     """w2( SiLU(w1 h) * (w3 h) ), no biases ([AIT] "Architecture": SwiGLU
-    FFN; [MNN] "Conversion details": weights w1, w2, w3)."""
-    a = h @ _f64(W[f"{prefix}.feed_forward.w1.weight"]).T
-    b = h @ _f64(W[f"{prefix}.feed_forward.w3.weight"]).T
-    return (silu(a) * b) @ _f64(W[f"{prefix}.feed_forward.w2.weight"]).T
+    FFN; [MNN] "Conversion details": weights w1, w2, w3).  With int8
+    projections, the SwiGLU product reaches w2 as bf16 values."""
+    a = linear(h, W[f"{prefix}.feed_forward.w1.weight"], quant)
+    b = linear(h, W[f"{prefix}.feed_forward.w3.weight"], quant)
+    return linear(silu(a) * b, W[f"{prefix}.feed_forward.w2.weight"], quant, held="bf16")
 
 
-def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=None):
+def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=None, quant=None):
     """One S3-DiT transformer block over a single sample's sequence x [S, D].
 
     Sandwich-norm block ([AIT] "Architecture"; [MNN] "Conversion details":
@@ -249,7 +263,9 @@ def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=No
     (context refiner, [AIT] "Architecture"): scales 1 and gates 1.
     ``rows`` restricts the output (and the queries) to those rows; keys and
     values still come from every row.  ``taps`` (a dict), if given, receives
-    the w2 output under "ffn_out" (observation only).
+    the w2 output under "ffn_out" (observation only).  ``quant`` "int8"
+    runs the seven projections as oracle.quant defines (the attention output
+    reaches to_out as bf16 values).
     """
     D, H, hd, eps = cfg.hidden, cfg.n_heads, cfg.head_dim, cfg.norm_eps
     x = _f64(x)
@@ -260,19 +276,19 @@ def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=No
     qrows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
 
     h = rms_norm(x, W[f"{prefix}.attention_norm1.weight"], eps) * scale_a
-    q = h[qrows] @ _f64(W[f"{prefix}.attention.to_q.weight"]).T
-    k = h @ _f64(W[f"{prefix}.attention.to_k.weight"]).T
-    v = h @ _f64(W[f"{prefix}.attention.to_v.weight"]).T
+    q = linear(h[qrows], W[f"{prefix}.attention.to_q.weight"], quant)
+    k = linear(h, W[f"{prefix}.attention.to_k.weight"], quant)
+    v = linear(h, W[f"{prefix}.attention.to_v.weight"], quant)
     q = rms_norm(q.reshape(-1, H, hd), W[f"{prefix}.attention.norm_q.weight"], eps)
     k = rms_norm(k.reshape(-1, H, hd), W[f"{prefix}.attention.norm_k.weight"], eps)
     q = apply_rope(q, _f64(cos)[qrows], _f64(sin)[qrows])
     k = apply_rope(k, cos, sin)
     o = attention(q, k, v.reshape(-1, H, hd)).reshape(-1, D)
-    a = o @ _f64(W[f"{prefix}.attention.to_out.0.weight"]).T
+    a = linear(o, W[f"{prefix}.attention.to_out.0.weight"], quant, held="bf16")
     x1 = x[qrows] + gate_a * rms_norm(a, W[f"{prefix}.attention_norm2.weight"], eps)
 
     h2 = rms_norm(x1, W[f"{prefix}.ffn_norm1.weight"], eps) * scale_f
-    f = swiglu_ffn(W, prefix, h2)
+    f = swiglu_ffn(W, prefix, h2, quant)
     if taps is not None:
         taps["ffn_out"] = f
     return x1 + gate_f * rms_norm(f, W[f"{prefix}.ffn_norm2.weight"], eps)
@@ -308,7 +324,7 @@ def final_layer(cfg: ModelConfig, W, x_img, c):
     return z @ _f64(W["final_layer.linear.weight"]).T + _f64(W["final_layer.linear.bias"])
 
 
-def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak=None):
+def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak=None, quant=None):
     """Forward of one sample: latent [C, Hl, Wl], caption features [L, 2560],
     scalar model time t -> raw model output [C, Hl, Wl].
 
@@ -317,6 +333,8 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak
     blocks over [image; caption], then the final layer on the image tokens.
     ``capture`` (a dict) receives the residual after each stage; ``ffn_peak``
     (a list) receives max |w2 output| of each block (observation only).
+    ``quant`` selects the block projections' arithmetic (see ``block``);
+    embedders, conditioning and the final layer stay in float64.
     """
     C, Hl, Wl = np.shape(latent)
     Hp, Wp = Hl // cfg.patch, Wl // cfg.patch
@@ -340,15 +358,15 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak
         mod = block_modulation(W, prefix, c) if modulated else None
         taps = {} if ffn_peak is not None else None
         if prefix.startswith("noise_refiner"):
-            x_img = block(cfg, W, prefix, x_img, cos_img, sin_img, mod, taps=taps)
+            x_img = block(cfg, W, prefix, x_img, cos_img, sin_img, mod, taps=taps, quant=quant)
             out = x_img
         elif prefix.startswith("context_refiner"):
-            y = block(cfg, W, prefix, y, cos_cap, sin_cap, None, taps=taps)
+            y = block(cfg, W, prefix, y, cos_cap, sin_cap, None, taps=taps, quant=quant)
             out = y
         else:
             if x is None:
                 x = np.concatenate([x_img, y])
-            x = block(cfg, W, prefix, x, cos_all, sin_all, mod, taps=taps)
+            x = block(cfg, W, prefix, x, cos_all, sin_all, mod, taps=taps, quant=quant)
             out = x
         if ffn_peak is not None:
             ffn_peak.append(float(np.max(np.abs(taps["ffn_out"]))))
@@ -363,7 +381,7 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak
     return unpatchify(o, C, Hl, Wl, cfg.patch)
 
 
-def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None, ffn_peak=None):
+def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None, ffn_peak=None, quant=None):
     """Batched forward: latent [B, C, Hl, Wl], caption_feats a list of B
     arrays [L_b, 2560] (exact lengths, no padding: [AIT] "Architecture",
     "padding dropped"), t [B] -> [B, C, Hl, Wl].  Samples are independent.
@@ -374,5 +392,5 @@ def forward(cfg: ModelConfig, W, latent, caption_feats, t, captures=None, ffn_pe
     outs = []
     for b in range(latent.shape[0]):
         cap = captures[b] if captures is not None else None
-        outs.append(forward_sample(cfg, W, latent[b], caption_feats[b], t[b], cap, ffn_peak))
+        outs.append(forward_sample(cfg, W, latent[b], caption_feats[b], t[b], cap, ffn_peak, quant))
     return np.stack(outs)
