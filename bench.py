@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 METRIC = "DiT forward tokens/sec at 1024^2 (4096+512 tok), 1 MI355X; MFMA util %"
 PEAK_BF16 = 2.5e15  # dense bf16 MFMA, FLOP/s
+PEAK_INT8 = 5.0e15  # dense int8 MFMA, OP/s
 PEAK_HBM = 8.0e12   # bytes/s
 
 
@@ -50,12 +51,16 @@ def stage_rows(model, n_img, lens):
     return out
 
 
-def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
+def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256, int8=False):
     """Algorithmic FLOPs of the MFMA classes and algorithmic HBM bytes of the
-    bandwidth-bound classes, per forward, keyed by the engine's profile classes."""
+    bandwidth-bound classes, per forward, keyed by the engine's profile classes.
+    int8: the block projections take int8 activations (1 B/elem written by
+    the norms; the attention output and SwiGLU product are read as bf16 and
+    written as int8 by the quant class)."""
     D, F = model["hidden"], model["ffn"]
     w = {k: 0.0 for k in ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
-                          "pre_norm", "post_norm", "embed", "final_layer", "conditioning")}
+                          "pre_norm", "post_norm", "embed", "final_layer", "conditioning", "quant")}
+    hb = 1.0 if int8 else 2.0  # bytes per element of a normalised block input
     stages = stage_rows(model, n_img, lens)
     prev = None
     for i, (stage, rows) in enumerate(stages):
@@ -68,11 +73,14 @@ def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
         w["attention"] += sum(4.0 * r * r * D for r in rows)
         # pre-norm only where not fused into the previous block's last kernel
         if prev != stage:
-            w["pre_norm"] += M * 6.0 * D
-        # two post-norms: read y bf16, read+write x fp32, write next h bf16 (12 B/elem);
-        # the last one of a stage without a fused follow-up skips the h write (10 B/elem)
+            w["pre_norm"] += M * (4.0 + hb) * D
+        # two post-norms: read y bf16, read+write x fp32, write next h (12 B/elem for bf16);
+        # the last one of a stage without a fused follow-up skips the h write (10 B/elem);
+        # before the final layer h is bf16 in either case
         nxt = stages[i + 1][0] if i + 1 < len(stages) else "final"
-        w["post_norm"] += M * 12.0 * D + M * (12.0 if (nxt == stage or nxt == "final") else 10.0) * D
+        w["post_norm"] += M * (10.0 + hb) * D + M * (10.0 + (2.0 if nxt == "final" else hb if nxt == stage else 0.0)) * D
+        if int8:
+            w["quant"] += M * 3.0 * (D + F)  # read bf16, write int8 (row scales are negligible)
         prev = stage
     T = sum(lens)
     w["embed"] = 2.0 * n_img * len(lens) * patch_dim * D + 2.0 * T * cap_dim * D
@@ -83,7 +91,45 @@ def work_per_forward(model, n_img, lens, cap_dim=2560, patch_dim=64, adaln=256):
 
 
 MFMA_CLASSES = ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention", "embed", "final_layer")
-HBM_CLASSES = ("pre_norm", "post_norm")
+INT8_CLASSES = ("gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2")  # with linear_int8 = 1
+HBM_CLASSES = ("pre_norm", "post_norm", "quant")
+
+
+def summarize(stats, steps, work, int8=False):
+    """Per-class time, achieved rate and fraction of the class's peak; and the
+    roofline entry of the class with the most time."""
+    kernels = {}
+    for name, (launches, ms) in stats.items():
+        if launches == 0:
+            continue
+        per_fwd_ms = ms / steps
+        entry = {"ms_per_forward": round(per_fwd_ms, 4), "launches_per_forward": launches // steps,
+                 "avg_launch_us": round(ms / launches * 1e3, 2)}
+        if name in MFMA_CLASSES:
+            peak = PEAK_INT8 if (int8 and name in INT8_CLASSES) else PEAK_BF16
+            ach = work[name] / (per_fwd_ms * 1e-3)
+            entry.update(achieved=round(ach / 1e12, 2), unit="TOP/s" if peak == PEAK_INT8 else "TFLOP/s",
+                         frac=round(ach / peak, 4))
+        elif name in HBM_CLASSES:
+            ach = work[name] / (per_fwd_ms * 1e-3)
+            entry.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / PEAK_HBM, 4))
+        kernels[name] = entry
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_forward"])
+    d = kernels[dom]
+    launches_dom = stats[dom][0] / steps
+    per_launch = work[dom] / launches_dom if launches_dom else 0.0
+    avg_s = d["avg_launch_us"] * 1e-6
+    if dom in HBM_CLASSES:
+        roof = {"bound": "hbm", "achieved": round(per_launch / avg_s / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        peak = PEAK_INT8 if (int8 and dom in INT8_CLASSES) else PEAK_BF16
+        roof = {"bound": "mfma", "achieved": round(per_launch / avg_s / 1e12, 2), "peak": peak / 1e12,
+                "unit": "TOP/s" if peak == PEAK_INT8 else "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["work_per_launch"] = per_launch
+    return kernels, roof, dom
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -206,6 +252,48 @@ def guided_step(dit, wl, lat, caps, lens, n_img, stream, steps=3, neg_len=32, gu
             "update_bytes_per_element": 16}
 
 
+# ---------------------------------------------------------------- int8 variant
+
+def int8_forward(args, wl, model, lat, caps, lens, t, n_img, tokens, bf16_ms):
+    """The same forward with the block projections on int8 codes (weights per
+    output row, activations per token): its own engine, K timed forwards,
+    then K profiled ones."""
+    import torch
+
+    import synthetic
+    from diffusion_transformer_image_amd import binding
+    steps = args.int8_steps
+    cfg = binding.config(max_batch=lat.shape[0], max_image_tokens=n_img, max_caption_tokens=max(lens),
+                         linear_int8=1, **model)
+    W = synthetic.SyntheticWeights(binding.manifest(cfg), seed=wl["seed"], outlier_log2=wl.get("outlier_log2"))
+    dit = binding.DiT(cfg, W.items_parallel(as_bits=True))
+    out = torch.empty_like(lat)
+    for _ in range(max(args.warmup, 1)):
+        dit.forward(lat, caps, lens, t, out)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for _ in range(steps):
+        dit.forward(lat, caps, lens, t, out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    assert torch.isfinite(out).all().item(), "non-finite int8 output"
+    dit.profile(True)
+    for _ in range(steps):
+        dit.forward(lat, caps, lens, t, out)
+    torch.cuda.synchronize()
+    stats = dit.profile_read()
+    dit.profile(False)
+    dit.close()
+    kernels, roof, _ = summarize(stats, steps, work_per_forward(model, n_img, lens, int8=True), int8=True)
+    ms = wall * 1e3 / steps
+    log(f"int8 forward: {ms:.2f} ms")
+    return {"workload": "the same forward with the 7 projections of every block on int8 codes "
+                        "(per-output-row weight scales, per-token activation scales, exact int32 sums)",
+            "steps": steps, "ms_per_step": round(ms, 3), "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+            "speedup_vs_bf16": round(bf16_ms / ms, 3), "dtype": "int8 projections, bf16 attention",
+            "roofline": roof, "kernels": kernels}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -217,6 +305,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cfg-steps", type=int, default=3, metavar="K",
                     help="also time K classifier-free-guided steps (0: skip)")
+    ap.add_argument("--int8-steps", type=int, default=10, metavar="K",
+                    help="also time K forwards with int8 block projections (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also launch one plain device copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -298,35 +388,8 @@ def main():
         log(f"copy calibration: {args.copy_calibration} MiB read + written")
 
     work = work_per_forward(model, n_img, lens)
-    kernels = {}
-    for name, (launches, ms) in stats.items():
-        if launches == 0:
-            continue
-        per_fwd_ms = ms / args.steps
-        entry = {"ms_per_forward": round(per_fwd_ms, 4), "launches_per_forward": launches // args.steps,
-                 "avg_launch_us": round(ms / launches * 1e3, 2)}
-        if name in MFMA_CLASSES:
-            ach = work[name] / (per_fwd_ms * 1e-3)
-            entry.update(achieved=round(ach / 1e12, 2), unit="TFLOP/s", frac=round(ach / PEAK_BF16, 4))
-        elif name in HBM_CLASSES:
-            ach = work[name] / (per_fwd_ms * 1e-3)
-            entry.update(achieved=round(ach / 1e9, 1), unit="GB/s", frac=round(ach / PEAK_HBM, 4))
-        kernels[name] = entry
-    dom = max(kernels, key=lambda k: kernels[k]["ms_per_forward"])
-    d = kernels[dom]
-    launches_dom = stats[dom][0] / args.steps
-    per_launch = work[dom] / launches_dom if launches_dom else 0.0
-    avg_s = d["avg_launch_us"] * 1e-6
-    if dom in HBM_CLASSES:
-        roof = {"bound": "hbm", "achieved": round(per_launch / avg_s / 1e9, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": round(per_launch / avg_s / 1e12, 2), "peak": PEAK_BF16 / 1e12,
-                "unit": "TFLOP/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    kernels, roof, dom = summarize(stats, args.steps, work)
     roof["traffic"] = committed_traffic(dom, args.workload)
-    roof["kernel"] = dom
-    roof["work_per_launch"] = per_launch
 
     ms_per_step = wall * 1e3 / args.steps
     fwd_flops = sum(work[k] for k in MFMA_CLASSES)
@@ -353,10 +416,12 @@ def main():
     }
     if cfg_step is not None:
         result["cfg_step"] = cfg_step
+    dit.close()
+    if args.int8_steps > 0:
+        result["int8_forward"] = int8_forward(args, wl, model, lat, caps, lens, t, n_img, tokens, ms_per_step)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, model) if B == 1 else None
-    dit.close()
     print(json.dumps(result), flush=True)
 
 

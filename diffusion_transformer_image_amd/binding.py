@@ -47,7 +47,7 @@ class Config(ctypes.Structure):
         ("t_scale", ctypes.c_float), ("max_period", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("final_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_image_tokens", ctypes.c_int32), ("max_caption_tokens", ctypes.c_int32),
-        ("batch_invariant", ctypes.c_int32),
+        ("batch_invariant", ctypes.c_int32), ("linear_int8", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -92,6 +92,8 @@ SIGNATURES = {
     "zimg_row_layout": (_I32, [_I32, _I32, _I32P, _I32P, _I32P, _I32P]),
     "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
     "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
+    "zimg_gemm_i8": (_I32, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
+    "zimg_quantize_rows": (_I32, [_P, _I32, _I64, _P, _I64, _P, _I32, _I32, _P]),
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
     "zimg_cfg_euler_step": (_I32, [_P, _P, _P, ctypes.c_float, ctypes.c_float, _I64, _P]),
     "zimg_dit_profile": (_I32, [_P, _I32]),
@@ -304,6 +306,28 @@ def gemm_bf16(A, W, C, epilogue=EPI_BF16, bias=None, stream=None):
     _check(lib().zimg_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), _ptr(C), C.stride(0), M, N, K,
                                 epilogue, _ptr(bias) if bias is not None else None, _stream(stream)))
     return C
+
+
+def gemm_i8(A, sa, W, sw, C, epilogue=EPI_BF16, bias=None, stream=None):
+    """C = epilogue((A W^T) * sa[:, None] * sw[None, :]) on torch CUDA tensors
+    (A, W int8 codes; sa, sw fp32 row scales; C bf16 or fp32)."""
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().zimg_gemm_i8(_ptr(A), A.stride(0), _ptr(sa), _ptr(W), W.stride(0), _ptr(sw), _ptr(C), C.stride(0),
+                              M, N, K, epilogue, _ptr(bias) if bias is not None else None, _stream(stream)))
+    return C
+
+
+def quantize_rows(x, q, scale, stream=None):
+    """Per-row int8 codes q and scales of x (torch CUDA fp32 or bf16 rows)."""
+    import torch
+    rows, K = x.shape
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"quantize_rows takes fp32 or bf16 rows, got {x.dtype}")
+    dt = ZIMG_BF16 if x.dtype == torch.bfloat16 else ZIMG_F32
+    _check(lib().zimg_quantize_rows(_ptr(x), dt, x.stride(0), _ptr(q), q.stride(0), _ptr(scale), rows, K,
+                                    _stream(stream)))
+    return q, scale
 
 
 def cfg_euler_step(x, out_cond, out_uncond, guidance, dt, stream=None):

@@ -35,6 +35,43 @@ ZI_DEV f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_i32_32x32x32_i8: each lane supplies 16 int8 of A (row l % 32) and
+// 16 of B (column l % 32) in the same positions of K, so products pair A
+// and B values of the same k whatever order the unit takes K in; the int32
+// sums are exact.  Accumulator layout as for mfma32.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+ZI_DEV i32x16 mfma32_i8(const bf16x8& a, const bf16x8& b, const i32x16& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// fp32 product rounded on its own: the optimizer cannot fuse it into a later
+// add (HIP contracts a*b + c into one fma across statements by default).
+ZI_DEV float mul_rn(float a, float b) {
+  float r;
+  asm("v_mul_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Symmetric per-row int8 quantization of the block projections' operands:
+// for a row with amax = max |v|, scale = amax / 127 and inv = 127 / amax
+// (each one correctly rounded fp32 division), code = rint(v * inv) clamped
+// to [-127, 127] (rint: half to even); an all-zero row has scale 0, codes 0.
+// Callers pass amax as NaN when the row holds a NaN or an infinity, which
+// gives a NaN scale, so the fault stays visible downstream.
+ZI_DEV void quant_params(float amax, float& scale, float& inv) {
+  const bool z = amax == 0.f;
+  scale = z ? 0.f : __fdiv_rn(amax, 127.0f);
+  inv = z ? 0.f : __fdiv_rn(127.0f, amax);
+}
+ZI_DEV uint32_t quant_code(float v, float inv) {
+  const float q = fminf(fmaxf(rintf(__fmul_rn(v, inv)), -127.f), 127.f);
+  return (uint32_t)((int)q) & 0xffu;
+}
+ZI_DEV uint32_t quant4(float a, float b, float c, float d, float inv) {
+  return quant_code(a, inv) | (quant_code(b, inv) << 8) | (quant_code(c, inv) << 16) | (quant_code(d, inv) << 24);
+}
+
 // Barrier that publishes direct global->LDS loads: each wave first waits for
 // its own outstanding loads (vmcnt), then all waves meet.  Written out
 // explicitly because the compiler does not always place that wait before a

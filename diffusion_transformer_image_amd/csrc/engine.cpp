@@ -195,6 +195,7 @@ int check_config(const zimg_dit_config* c) {
   if (c->max_caption_tokens < 1 || c->max_caption_tokens > 512)
     return set_err(ZIMG_EUNSUPPORTED, "max_caption_tokens must be 1..512 (the caption limit of the model)");
   if (c->batch_invariant != 0 && c->batch_invariant != 1) return set_err(ZIMG_EINVAL, "batch_invariant must be 0 or 1");
+  if (c->linear_int8 != 0 && c->linear_int8 != 1) return set_err(ZIMG_EINVAL, "linear_int8 must be 0 or 1");
   return ZIMG_OK;
 }
 
@@ -284,6 +285,10 @@ struct zimg_dit {
   struct BlockW {
     bf16_t *wqkv = nullptr, *wo = nullptr, *w13 = nullptr, *w2 = nullptr;
     float *an1 = nullptr, *an2 = nullptr, *fn1 = nullptr, *fn2 = nullptr, *nq = nullptr, *nk = nullptr;
+    // int8 projections: codes of the same matrices (same row order) and one
+    // scale per row; the bf16 copies are released once these are made
+    int8_t *qqkv = nullptr, *qo = nullptr, *q13 = nullptr, *q2 = nullptr;
+    float *sqkv = nullptr, *so = nullptr, *s13 = nullptr, *s2 = nullptr;
   };
   std::vector<BlockW> bw;
   bf16_t *t1w = nullptr, *t2w = nullptr, *cap_w = nullptr, *x_w = nullptr, *fin_w = nullptr, *ada_w = nullptr;
@@ -305,6 +310,10 @@ struct zimg_dit {
   bf16_t *h = nullptr, *qkv = nullptr, *vT = nullptr, *o = nullptr, *y = nullptr, *g = nullptr, *xin = nullptr,
          *capn = nullptr;
   float *temb = nullptr, *hmid = nullptr, *cvec = nullptr, *mod = nullptr;
+  // int8 projections: the block inputs h / h2 (hq), the attention output (oq)
+  // and the SwiGLU product (gq) as int8 codes with one scale per row
+  int8_t *hq = nullptr, *oq = nullptr, *gq = nullptr;
+  float *hs = nullptr, *os = nullptr, *gs = nullptr;
   // the blocks' four norm weights, [n_blocks][4][D] (an1, an2, fn1, fn2), and
   // per forward those weights with the sample's modulation folded in,
   // [max_batch][4 n_blocks + 1][D] (the last slot: the final layer's 1 + s)
@@ -339,7 +348,7 @@ struct zimg_dit {
   std::vector<void*> allocations;
 
   // per-kernel-class timing with HIP events on the forward's stream
-  enum { K_QKV, K_OUT, K_W13, K_W2, K_ATTN, K_PRENORM, K_POSTNORM, K_EMBED, K_FINAL, K_COND, K_COUNT };
+  enum { K_QKV, K_OUT, K_W13, K_W2, K_ATTN, K_PRENORM, K_POSTNORM, K_EMBED, K_FINAL, K_COND, K_QUANT, K_COUNT };
   struct Prof {
     bool on = false;
     std::vector<hipEvent_t> ev;  // pairs (start, stop)
@@ -393,6 +402,15 @@ struct zimg_dit {
     if (e != hipSuccess) return set_err(ZIMG_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
     *p = (T*)q;
     return ZIMG_OK;
+  }
+
+  void dfree(void* p) {
+    for (size_t i = 0; i < allocations.size(); ++i)
+      if (allocations[i] == p) {
+        (void)hipFree(p);
+        allocations.erase(allocations.begin() + i);
+        return;
+      }
   }
 
   ~zimg_dit() {
@@ -456,6 +474,16 @@ int zimg_dit::allocate() {
     w.fn2 = normw + (int64_t)(4 * i + 3) * D;
     ALLOC(w.nq, 128);
     ALLOC(w.nk, 128);
+    if (c.linear_int8) {
+      ALLOC(w.qqkv, 3 * D * D);
+      ALLOC(w.qo, D * D);
+      ALLOC(w.q13, 2 * F * D);
+      ALLOC(w.q2, D * F);
+      ALLOC(w.sqkv, 3 * D);
+      ALLOC(w.so, D);
+      ALLOC(w.s13, 2 * F);
+      ALLOC(w.s2, D);
+    }
   }
 
   // slots, named as in the manifest
@@ -513,6 +541,14 @@ int zimg_dit::allocate() {
   ALLOC(o, S_max * D);
   ALLOC(y, S_max * D);
   ALLOC(g, S_max * F);
+  if (c.linear_int8) {
+    ALLOC(hq, S_max * D);
+    ALLOC(oq, S_max * D);
+    ALLOC(gq, S_max * F);
+    ALLOC(hs, S_max);
+    ALLOC(os, S_max);
+    ALLOC(gs, S_max);
+  }
   ALLOC(xin, img_rows_max * P);
   ALLOC(capn, cap_rows_max * c.cap_feat_dim);
   ALLOC(temb, (int64_t)c.max_batch * c.adaln_dim);
@@ -596,6 +632,23 @@ int zimg_dit::finalize() {
       ++nmiss;
     }
   if (nmiss) return set_err(ZIMG_EWEIGHT, "%d weight(s) missing: %s%s", nmiss, missing.c_str(), nmiss > 5 ? ", ..." : "");
+  if (cfg.linear_int8) {
+    // quantize every block projection per output row, then drop the bf16 copies
+    const int D = cfg.hidden, F = cfg.ffn;
+    for (BlockW& w : bw) {
+      HIP_TRY(zimg::launch_quant_rows(w.wqkv, 1, D, w.qqkv, D, w.sqkv, 3 * D, D, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.wo, 1, D, w.qo, D, w.so, D, D, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.w13, 1, D, w.q13, D, w.s13, 2 * F, D, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.w2, 1, F, w.q2, F, w.s2, D, F, nullptr));
+    }
+    HIP_TRY(hipDeviceSynchronize());
+    for (BlockW& w : bw) {
+      for (bf16_t** m : {&w.wqkv, &w.wo, &w.w13, &w.w2}) {
+        dfree(*m);
+        *m = nullptr;
+      }
+    }
+  }
   finalized = true;
   return ZIMG_OK;
 }
@@ -721,15 +774,23 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   // folded norm weights of this block: 0 attention pre, 1 attention post,
   // 2 FFN pre, 3 FFN post
   auto mref = [&](int chunk) { return zimg::VecRef{fold + (int64_t)(4 * bi + chunk) * D, fold_stride}; };
+  const bool i8 = c.linear_int8 != 0;
   if (!h_ready) {
-    zimg::PreNormArgs pa{x, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0};
+    zimg::PreNormArgs pa{x, mref(0), row_sample, h, r0, r1, D, c.norm_eps, 0, hq, hs};
     PROFILED(K_PRENORM, zimg::launch_pre_norm(pa, s));
   }
+  // operands of a projection: bf16, or int8 codes with per-row scales
   zimg::GemmArgs ga{};
-  ga.A = h + (int64_t)r0 * D;
-  ga.lda = D;
-  ga.W = w.wqkv;
-  ga.ldw = D;
+  auto operands = [&](const bf16_t* a16, const int8_t* a8, const float* sa, const bf16_t* w16, const int8_t* w8,
+                      const float* sw, int64_t ld) {
+    ga.i8 = i8;
+    ga.A = i8 ? (const void*)(a8 + (int64_t)r0 * ld) : (const void*)(a16 + (int64_t)r0 * ld);
+    ga.W = i8 ? (const void*)w8 : (const void*)w16;
+    ga.lda = ga.ldw = ld;
+    ga.ep.sa = i8 ? sa + r0 : nullptr;
+    ga.ep.sw = i8 ? sw : nullptr;
+  };
+  operands(h, hq, hs, w.wqkv, w.qqkv, w.sqkv, D);
   ga.M = M;
   ga.N = 3 * D;
   ga.K = D;
@@ -766,8 +827,8 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
                     split.ws};
   PROFILED(K_ATTN, zimg::launch_attention(aa, s));
 
-  ga.A = o + (int64_t)r0 * D;
-  ga.W = w.wo;
+  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(o + (int64_t)r0 * D, 1, D, oq + (int64_t)r0 * D, D, os + r0, M, D, s));
+  operands(o, oq, os, w.wo, w.qo, w.so, D);
   ga.N = D;
   ga.ep.C = y + (int64_t)r0 * D;
   ga.ep.ldc = D;
@@ -790,10 +851,11 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   pn.h = h;
   pn.D = D;
   pn.eps = c.norm_eps;
+  pn.hq = hq;
+  pn.hs = hs;
   PROFILED(K_POSTNORM, zimg::launch_post_norm(pn, s));
 
-  ga.A = h + (int64_t)r0 * D;
-  ga.W = w.w13;
+  operands(h, hq, hs, w.w13, w.q13, w.s13, D);
   ga.N = 2 * F;
   ga.epi = zimg::EPI_SWIGLU;
   ga.ep.C = g + (int64_t)r0 * F;
@@ -802,10 +864,8 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.split = gemm_split();
   PROFILED(K_W13, zimg::launch_gemm(ga, s));
 
-  ga.A = g + (int64_t)r0 * F;
-  ga.lda = F;
-  ga.W = w.w2;
-  ga.ldw = F;
+  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(g + (int64_t)r0 * F, 1, F, gq + (int64_t)r0 * F, F, gs + r0, M, F, s));
+  operands(g, gq, gs, w.w2, w.q2, w.s2, F);
   ga.N = D;
   ga.K = F;
   ga.epi = zimg::EPI_BF16;
@@ -826,6 +886,8 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
     pn.wn = zimg::VecRef{fold + (int64_t)(4 * blocks.size()) * D, fold_stride};
     pn.next_kind = 1;
     pn.next_eps = c.final_eps;
+    pn.hq = nullptr;  // the final layer takes bf16
+    pn.hs = nullptr;
   } else {
     pn.n0 = pn.n1 = 0;
   }
@@ -1179,6 +1241,47 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
   return ZIMG_OK;
 }
 
+int zimg_gemm_i8(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw, const float* sw, void* C,
+                 int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, const float* bias, void* stream) {
+  g_last_error.clear();
+  zimg::GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W = W;
+  g.ldw = ldw;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.i8 = 1;
+  g.epi = epilogue;
+  g.ep.C = C;
+  g.ep.ldc = ldc;
+  g.ep.bias = bias;
+  g.ep.sa = sa;
+  g.ep.sw = sw;
+  g.role = zimg::ROLE_ANY;
+  if (epilogue == zimg::EPI_UNPATCH || epilogue == zimg::EPI_QKV_ROPE)
+    return set_err(ZIMG_EUNSUPPORTED, "epilogue %d is internal", epilogue);
+  if (const char* m = zimg::gemm_check(g)) return set_err(ZIMG_EINVAL, "%s", m);
+  const int64_t need = epilogue == zimg::EPI_SWIGLU ? N / 2 : N;
+  if (ldc < need) return set_err(ZIMG_EINVAL, "ldc %lld smaller than the output width %lld", (long long)ldc, (long long)need);
+  HIP_TRY(zimg::launch_gemm(g, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
+int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                       int32_t rows, int32_t K, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || K <= 0 || K % 8 || K > 16384) return set_err(ZIMG_EINVAL, "need rows >= 0 and K a multiple of 8 in 8..16384");
+  if (x_dtype != ZIMG_F32 && x_dtype != ZIMG_BF16) return set_err(ZIMG_EINVAL, "unknown dtype %d", x_dtype);
+  if (ldx < K || ldq < K || ldx % 8 || ldq % 8) return set_err(ZIMG_EINVAL, "ldx, ldq must be multiples of 8 and >= K");
+  if (rows > 0 && (!x || !q || !scale)) return set_err(ZIMG_EINVAL, "NULL buffer");
+  const uintptr_t xa = (uintptr_t)x, qa = (uintptr_t)q;
+  if (rows > 0 && ((xa & 15) || (qa & 7))) return set_err(ZIMG_EINVAL, "x must be 16-byte and q 8-byte aligned");
+  HIP_TRY(zimg::launch_quant_rows(x, x_dtype == ZIMG_BF16, ldx, q, ldq, scale, rows, K, (hipStream_t)stream));
+  return ZIMG_OK;
+}
+
 int zimg_dit_profile(zimg_dit* h, int32_t enable) {
   g_last_error.clear();
   if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
@@ -1205,7 +1308,7 @@ int zimg_dit_profile(zimg_dit* h, int32_t enable) {
 int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats) {
   static const char* names[zimg_dit::K_COUNT] = {"gemm_qkv", "gemm_out", "gemm_w13_swiglu", "gemm_w2", "attention",
                                                  "pre_norm", "post_norm", "embed", "final_layer",
-                                                 "conditioning"};
+                                                 "conditioning", "quant"};
   g_last_error.clear();
   if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
   if (max_stats < 0 || (max_stats > 0 && !stats)) return set_err(ZIMG_EINVAL, "bad stats array");

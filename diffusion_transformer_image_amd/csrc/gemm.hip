@@ -1,9 +1,15 @@
-// bf16 MFMA GEMM for the S3-DiT projections: C = epilogue(A . W^T).
+// MFMA GEMM for the S3-DiT projections: C = epilogue(A . W^T).
 //
-// A [M, K] bf16 row-major (activations), W [N, K] bf16 row-major (a linear
-// layer's weight, out_features x in_features), fp32 accumulation on
-// v_mfma_f32_32x32x16_bf16.  Both operands are K-contiguous, which is what
-// the MFMA operand layout wants, so no transposition happens anywhere.
+// A [M, K] row-major (activations), W [N, K] row-major (a linear layer's
+// weight, out_features x in_features), both bf16 with fp32 accumulation on
+// v_mfma_f32_32x32x16_bf16, or both int8 with exact int32 accumulation on
+// v_mfma_i32_32x32x32_i8 (the int8 projections: per-row codes of A and W
+// with fp32 row scales, applied to the sums before the epilogue).  Both
+// operands are K-contiguous, which is what the MFMA operand layout wants, so
+// no transposition happens anywhere.  A 16-byte chunk holds 8 bf16 or 16
+// int8 values, and one MFMA consumes one chunk per lane of each operand in
+// either case, so the data movement below is the same for both types: it
+// counts K in bf16-sized units (an int8 row of K codes is K/2 units).
 //
 // Workgroup tile BM x BN, K-step 64, 512 threads = 8 waves (2 waves per
 // SIMD, so one wave's MFMAs cover the other's memory waits).  Operands go
@@ -36,6 +42,40 @@ constexpr int GROUP_M = 8;
 
 // Epilogue: element e = ii*4 + jj of subtile (i, j) of a wave is row
 // i*32 + ii*8 + lhalf*4 + jj, column j*32 + lrow of the wave tile.
+template <bool I8>
+struct AccOf {
+  using T = f32x16;
+};
+template <>
+struct AccOf<true> {
+  using T = i32x16;
+};
+
+// int8 operands: accumulator element (i, j, e) of a wave is the exact sum of
+// row rbase + i*32 + (e>>2)*8 + lhalf*4 + (e&3), column cbase + j*32 + lrow;
+// scale it by the row's and the column's scale (rows or columns past the
+// matrix read the last one; they are never stored).
+template <int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void scale_acc(const i32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                                          f32x16 (&out)[BM / WM / 32][BN / WN / 32], int m0, int n0, int M, int N,
+                                          const EpiArgs& ep) {
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  float cs[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) cs[j] = ep.sw[min(n0 + wn * WTN + j * 32 + lrow, N - 1)];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float rs = ep.sa[min(m0 + wm * WTM + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3), M - 1)];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) out[i][j][e] = mul_rn(mul_rn((float)acc[i][j][e], rs), cs[j]);
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI>
 __device__ __forceinline__ void epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0, int M, int N,
                                          const EpiArgs& ep) {
@@ -265,9 +305,21 @@ __device__ __forceinline__ void staged_bf16_epilogue(const f32x16 (&acc)[BM / WM
   }
 }
 
+template <int BM, int BN, int WM, int WN, int EPI>
+__device__ __forceinline__ void run_epilogue(f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0, int M, int N,
+                                             const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3) {
+  if constexpr (EPI == EPI_QKV_ROPE)
+    qkv_rope_epilogue<BM, BN, WM, WN>(acc, m0, n0, M, ep, s0, s1, s2, s3);
+  else if constexpr ((EPI == EPI_BF16 || EPI == EPI_SWIGLU) && BM == 256 && BN == 256)
+    staged_bf16_epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, ep, s0, s1, s2, s3);
+  else
+    epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
+}
+
 // ROLE only separates the symbols of the projections (qkv, out, w1|w3, w2,
-// embeds, final) so that profiles attribute time per projection.
-template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
+// embeds, final) so that profiles attribute time per projection.  I8: int8
+// operands (pointers, strides and K in bf16-sized units, see above).
+template <int BM, int BN, int WM, int WN, int EPI, int ROLE, bool I8>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                      const bf16_t* __restrict__ W, int64_t ldw,
                                                      int M, int N, int K, EpiArgs ep, int tiles_m,
@@ -336,11 +388,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
       __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kt * BK), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
   };
 
-  f32x16 acc[TM][TN];
+  using AccT = typename AccOf<I8>::T;
+  AccT acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TN; ++j) acc[i][j] = AccT{};
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int sw = (lrow >> 1) & 7;  // subtile bases are multiples of 32 rows
@@ -368,7 +421,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) {
+          if constexpr (I8)
+            acc[i][j] = mfma32_i8(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+          else
+            acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
+        }
       if (kk + 1 < BK / 16) {
         constexpr int PAIRS = (TM + TN) < (TM * TN) ? (TM + TN) : (TM * TN);
 #pragma unroll
@@ -399,24 +457,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   if (kt < KT) step(As0, Bs0, false, 0, As1, Bs1);
 
   if (is_split) {
-    // A split unit stores its fp32 partial (accumulator order, lanes
-    // contiguous) and stops; gemm_reduce_kernel sums the partials of each
-    // split tile in chunk order and runs the epilogue.
+    // A split unit stores its partial (accumulator order, lanes contiguous;
+    // int8: the int32 sums, bit for bit) and stops; the reduce kernel sums
+    // the partials of each split tile in chunk order and runs the epilogue.
     float* part = ws + ((int64_t)tail_idx * nsplit + chunk) * (BM * BN);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part[((i * TN + j) * 16 + e) * NT + tid] = acc[i][j][e];
+        for (int e = 0; e < 16; ++e) {
+          if constexpr (I8)
+            part[((i * TN + j) * 16 + e) * NT + tid] = __int_as_float(acc[i][j][e]);
+          else
+            part[((i * TN + j) * 16 + e) * NT + tid] = acc[i][j][e];
+        }
     return;
   }
-  if constexpr (EPI == EPI_QKV_ROPE)
-    qkv_rope_epilogue<BM, BN, WM, WN>(acc, m0, n0, M, ep, As0, Bs0, As1, Bs1);
-  else if constexpr ((EPI == EPI_BF16 || EPI == EPI_SWIGLU) && BM == 256 && BN == 256)
-    staged_bf16_epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, ep, As0, Bs0, As1, Bs1);
-  else
-    epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep);
+  if constexpr (I8) {
+    f32x16 accf[TM][TN];
+    scale_acc<BM, BN, WM, WN>(acc, accf, m0, n0, M, N, ep);
+    run_epilogue<BM, BN, WM, WN, EPI>(accf, m0, n0, M, N, ep, As0, Bs0, As1, Bs1);
+  } else {
+    run_epilogue<BM, BN, WM, WN, EPI>(acc, m0, n0, M, N, ep, As0, Bs0, As1, Bs1);
+  }
 }
 
 // Sum of the nsplit partials of each split tile, in chunk order (so the
@@ -427,7 +491,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
 // the w1/w3 pair (j, j+1) together.
 constexpr int RED_PER_THREAD = 4;
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool I8>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs ep, int tiles_m, int tiles_n,
                                                           int full_tiles, int nsplit, const float* __restrict__ ws) {
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
@@ -456,12 +520,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
     }
   }
   // chunk-outer, so that all of a chunk's loads are in flight together
+  // (int8: the partials are int32 sums, added exactly)
   float v[RED_PER_THREAD] = {}, v3[RED_PER_THREAD] = {};
+  int vi[RED_PER_THREAD] = {}, v3i[RED_PER_THREAD] = {};
   for (int c = 0; c < nsplit; ++c, part += TILE_F)
 #pragma unroll
     for (int r = 0; r < RED_PER_THREAD; ++r) {
-      v[r] += part[qs[r]];
-      if constexpr (EPI == EPI_SWIGLU) v3[r] += part[qs[r] + 16 * NT];
+      if constexpr (I8) {
+        vi[r] += __float_as_int(part[qs[r]]);
+        if constexpr (EPI == EPI_SWIGLU) v3i[r] += __float_as_int(part[qs[r] + 16 * NT]);
+      } else {
+        v[r] += part[qs[r]];
+        if constexpr (EPI == EPI_SWIGLU) v3[r] += part[qs[r] + 16 * NT];
+      }
     }
 #pragma unroll
   for (int r = 0; r < RED_PER_THREAD; ++r) {
@@ -471,6 +542,11 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
     const int row = m0 + wm * WTM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
     const int col = n0 + wn * WTN + j * 32 + (lane & 31);
     if (row >= M || col >= N) continue;
+    if constexpr (I8) {
+      const float rs = ep.sa[row];
+      v[r] = mul_rn(mul_rn((float)vi[r], rs), ep.sw[col]);
+      if constexpr (EPI == EPI_SWIGLU) v3[r] = mul_rn(mul_rn((float)v3i[r], rs), ep.sw[col + 32]);
+    }
     if constexpr (EPI == EPI_SWIGLU) {
       const float s = v[r] / (1.0f + __expf(-v[r]));
       const int ocol = ((n0 + wn * WTN + j * 32) >> 1) + (lane & 31);
@@ -499,7 +575,7 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
 // rows staged in LDS (same swizzle as the tile epilogue) and handed to
 // qk_rope_unit; v written transposed straight from the registers (lanes
 // l and l + 32 hold 4 + 4 consecutive rows of one column).
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, bool I8>
 __global__ __launch_bounds__(256) void gemm_qkv_reduce_kernel(int M, EpiArgs ep, int tiles_m, int tiles_n,
                                                               int full_tiles, int nsplit, const float* __restrict__ ws) {
   static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "QKV epilogue tiling");
@@ -517,15 +593,35 @@ __global__ __launch_bounds__(256) void gemm_qkv_reduce_kernel(int M, EpiArgs ep,
   const int src_tid = (wm * WN + wn) * 64 + lane;
   const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F + src_tid;
   f32x16 acc[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) acc[j] = f32x16{};
-  for (int c = 0; c < nsplit; ++c, part += TILE_F)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[j][e] += part[((i * TN + j) * 16 + e) * NT];
-  const int sec = n0 / ep.D;
   const int rs0 = wm * 128 + i * 32;  // slice's first row in the tile
+  if constexpr (I8) {
+    i32x16 ai[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) ai[j] = i32x16{};
+    for (int c = 0; c < nsplit; ++c, part += TILE_F)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ai[j][e] += __float_as_int(part[((i * TN + j) * 16 + e) * NT]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float cs = ep.sw[n0 + wn * 64 + j * 32 + lrow];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float rsc = ep.sa[min(m0 + rs0 + (e >> 2) * 8 + lhalf * 4 + (e & 3), M - 1)];
+        acc[j][e] = mul_rn(mul_rn((float)ai[j][e], rsc), cs);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[j] = f32x16{};
+    for (int c = 0; c < nsplit; ++c, part += TILE_F)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] += part[((i * TN + j) * 16 + e) * NT];
+  }
+  const int sec = n0 / ep.D;
   if (sec < 2) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -590,38 +686,42 @@ int choose_split(int T, int KT, int tile_bytes, const GemmSplit& sp) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, int ROLE>
+template <int BM, int BN, int WM, int WN, int EPI, int ROLE, bool I8>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   static_assert(2 * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int T = tiles_m * tiles_n;
   constexpr int LDS_BYTES = 2 * (BM + BN) * BK * 2;
+  constexpr int U = I8 ? 2 : 1;  // elements per bf16-sized unit
+  const int K = g.K / U;
   GemmSplit sp = g.split;
   sp.n_cu *= (160 * 1024) / LDS_BYTES;  // workgroups resident at once
-  const int nsplit = choose_split(T, g.K / BK, BM * BN * 4, sp);
+  const int nsplit = choose_split(T, K / BK, BM * BN * 4, sp);
   const int full = nsplit > 1 ? T - T % sp.n_cu : T;
   const int units = full + (T - full) * nsplit;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE>), dim3(units), dim3(NT), 0, s, g.A, g.lda, g.W,
-                     g.ldw, g.M, g.N, g.K, g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE, I8>), dim3(units), dim3(NT), 0, s,
+                     (const bf16_t*)g.A, g.lda / U, (const bf16_t*)g.W, g.ldw / U, g.M, g.N, K, g.ep, tiles_m,
+                     tiles_n, full, nsplit, g.split.ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   if constexpr (EPI == EPI_QKV_ROPE) {
-    hipLaunchKernelGGL((gemm_qkv_reduce_kernel<BM, BN, WM, WN>), dim3((T - full) * 8), dim3(256), 0, s, g.M, g.ep,
-                       tiles_m, tiles_n, full, nsplit, g.split.ws);
+    hipLaunchKernelGGL((gemm_qkv_reduce_kernel<BM, BN, WM, WN, I8>), dim3((T - full) * 8), dim3(256), 0, s, g.M,
+                       g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
     return hipGetLastError();
   }
   constexpr int SLOTS = (EPI == EPI_SWIGLU) ? BM * BN / 2 : BM * BN;
   static_assert(SLOTS % (256 * RED_PER_THREAD) == 0, "reduce grid");
-  hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WM, WN, EPI>), dim3((T - full) * (SLOTS / (256 * RED_PER_THREAD))),
-                     dim3(256), 0, s, g.M, g.N, g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
+  hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WM, WN, EPI, I8>),
+                     dim3((T - full) * (SLOTS / (256 * RED_PER_THREAD))), dim3(256), 0, s, g.M, g.N, g.ep, tiles_m,
+                     tiles_n, full, nsplit, g.split.ws);
   return hipGetLastError();
 }
 
-template <int EPI, int ROLE>
+template <int EPI, int ROLE, bool I8 = false>
 hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
-  if (g.N % 256 == 0) return launch_cfg<256, 256, 2, 4, EPI, ROLE>(g, s);
-  if (g.N % 128 == 0) return launch_cfg<256, 128, 4, 2, EPI, ROLE>(g, s);
-  return launch_cfg<256, 64, 8, 1, EPI, ROLE>(g, s);
+  if (g.N % 256 == 0) return launch_cfg<256, 256, 2, 4, EPI, ROLE, I8>(g, s);
+  if (g.N % 128 == 0) return launch_cfg<256, 128, 4, 2, EPI, ROLE, I8>(g, s);
+  return launch_cfg<256, 64, 8, 1, EPI, ROLE, I8>(g, s);
 }
 
 }  // namespace
@@ -647,14 +747,37 @@ const char* gemm_check(const GemmArgs& g) {
       ((g.role == ROLE_OUT || g.role == ROLE_W2) && g.epi != EPI_BF16) ||
       (g.role == ROLE_EMBED && g.epi != EPI_F32_BIAS) || (g.role == ROLE_FINAL && g.epi != EPI_UNPATCH))
     return "gemm: role and epilogue disagree";
+  if (g.i8) {
+    if (g.K % 128) return "gemm: int8 operands need K a multiple of 128";
+    if (g.N % 256) return "gemm: int8 operands need N a multiple of 256";
+    if ((g.lda % 16) || (g.ldw % 16) || ((uintptr_t)g.A & 15) || ((uintptr_t)g.W & 15))
+      return "gemm: int8 operands need lda, ldw multiples of 16 and 16-byte aligned A, W";
+    if (!g.ep.sa || !g.ep.sw) return "gemm: int8 operands need row scales sa and sw";
+    if (g.epi == EPI_UNPATCH || g.role == ROLE_EMBED || g.role == ROLE_FINAL)
+      return "gemm: int8 operands serve the block projections only";
+  }
   return nullptr;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (g.i8) {  // 256 x 256 tiles only (N % 256 == 0)
+    switch (g.role) {
+      case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_QKV_ROPE, ROLE_QKV, true>(g, s);
+      case ROLE_OUT: return launch_cfg<256, 256, 2, 4, EPI_BF16, ROLE_OUT, true>(g, s);
+      case ROLE_W13: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_W13, true>(g, s);
+      case ROLE_W2: return launch_cfg<256, 256, 2, 4, EPI_BF16, ROLE_W2, true>(g, s);
+      default: break;
+    }
+    switch (g.epi) {
+      case EPI_BF16: return launch_cfg<256, 256, 2, 4, EPI_BF16, ROLE_ANY, true>(g, s);
+      case EPI_F32_BIAS: return launch_cfg<256, 256, 2, 4, EPI_F32_BIAS, ROLE_ANY, true>(g, s);
+      default: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_ANY, true>(g, s);
+    }
+  }
   switch (g.role) {
-    case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_QKV_ROPE, ROLE_QKV>(g, s);
+    case ROLE_QKV: return launch_cfg<256, 256, 2, 4, EPI_QKV_ROPE, ROLE_QKV, false>(g, s);
     case ROLE_OUT: return launch_epi<EPI_BF16, ROLE_OUT>(g, s);
-    case ROLE_W13: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_W13>(g, s);
+    case ROLE_W13: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_W13, false>(g, s);
     case ROLE_W2: return launch_epi<EPI_BF16, ROLE_W2>(g, s);
     case ROLE_EMBED: return launch_epi<EPI_F32_BIAS, ROLE_EMBED>(g, s);
     case ROLE_FINAL: return launch_epi<EPI_UNPATCH, ROLE_FINAL>(g, s);
@@ -663,7 +786,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   switch (g.epi) {
     case EPI_BF16: return launch_epi<EPI_BF16, ROLE_ANY>(g, s);
     case EPI_F32_BIAS: return launch_epi<EPI_F32_BIAS, ROLE_ANY>(g, s);
-    case EPI_SWIGLU: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_ANY>(g, s);
+    case EPI_SWIGLU: return launch_cfg<256, 256, 2, 4, EPI_SWIGLU, ROLE_ANY, false>(g, s);
     default: return launch_epi<EPI_UNPATCH, ROLE_ANY>(g, s);
   }
 }

@@ -34,6 +34,11 @@ struct EpiArgs {
   bf16_t* vT;
   int trow0, S_pad, D;
   float eps;
+  // int8 operands: the int32 sum of column n of row m is scaled as
+  // (float(acc) * sa[m]) * sw[n] (row scales of A, of W's rows) before any
+  // epilogue
+  const float* sa;
+  const float* sw;
 };
 
 // Split of the last, partial wave of tiles along K (see gemm.hip): null
@@ -46,12 +51,15 @@ struct GemmSplit {
   int n_cu;       // compute units
 };
 
+// A and W are bf16, or (i8 = 1) int8 codes with the row scales in ep.sa /
+// ep.sw; lda, ldw, K count elements.
 struct GemmArgs {
-  const bf16_t* A;
+  const void* A;
   int64_t lda;
-  const bf16_t* W;
+  const void* W;
   int64_t ldw;
   int M, N, K;
+  int i8;
   int epi;
   EpiArgs ep;
   int role;
@@ -71,7 +79,8 @@ struct VecRef {
 };
 
 // h[r] = bf16( N(x[r]) * w[sample(r)] ) for rows r in [r0, r1), with N the
-// unit RMSNorm (kind 0) or the LayerNorm without affine (kind 1).
+// unit RMSNorm (kind 0) or the LayerNorm without affine (kind 1).  With hq
+// set, the row is written as int8 codes hq[r] and scale hs[r] instead.
 struct PreNormArgs {
   const float* x;
   VecRef w;
@@ -80,6 +89,8 @@ struct PreNormArgs {
   int r0, r1, D;
   float eps;
   int kind;
+  int8_t* hq;
+  float* hs;
 };
 hipError_t launch_pre_norm(const PreNormArgs& a, hipStream_t s);
 
@@ -99,6 +110,8 @@ struct PostNormArgs {
   bf16_t* h;
   int D;
   float eps;
+  int8_t* hq;  // as for PreNormArgs
+  float* hs;
 };
 hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s);
 
@@ -109,6 +122,11 @@ hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s);
 // mod_idx < 0, take normw alone), and 1 + s_final for the final slot.
 hipError_t launch_fold_mod(const float* mod, int64_t mod_stride, const float* normw, const int32_t* mod_idx,
                            int n_blocks, int n_mod, int D, int B, float* fold, hipStream_t s);
+
+// Rows of width K (K % 8 == 0, K <= 16384) of bf16 or fp32 values, row
+// stride ldx -> int8 codes (row stride ldq) and one scale per row.
+hipError_t launch_quant_rows(const void* x, int x_bf16, int64_t ldx, int8_t* q, int64_t ldq, float* scale, int rows,
+                             int K, hipStream_t s);
 
 // Caption features (fp32 or bf16 rows of width Dc) -> bf16 RMSNorm(x; w).
 hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t* out,

@@ -7,7 +7,8 @@
 // adaLN from the timestep embedding; "Z-Image-Turbo MNN (int8,
 // fp16-safe)", Conversion details: the to_out and w2 outputs feed an
 // RMSNorm).  Residual rows are fp32 and every reduction is fp32; activations
-// handed to the GEMMs are bf16.
+// handed to the GEMMs are bf16, or, for int8 projections, int8 codes with a
+// per-row scale (also the row quantizer for bf16 activations and weights).
 //
 // One 64-lane wave owns one row of the residual: lane l holds float4 number
 // l + 64 i of the row, so loads and stores are fully coalesced and the row
@@ -28,8 +29,10 @@ ZI_DEV void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
 }
 
 // normalise the row held in v[] (nv float4 per lane), scale by the folded
-// vector w and write bf16
-ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float eps, const float* w, bf16_t* h) {
+// vector w and write it: bf16 to h, or, when hq is set, int8 codes to hq and
+// the row's scale to *hs (per-row symmetric quantization of the fp32 values)
+ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float eps, const float* w, bf16_t* h,
+                       int8_t* hq, float* hs) {
   float mean = 0.f;
   if (kind == 1) {
     float s = 0.f;
@@ -46,6 +49,26 @@ ZI_DEV void norm_write(const float4* v, int nv, int lane, int D, int kind, float
       ss += a * a + b * b + c * c + d * d;
     }
   const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)D + eps);
+  if (hq) {
+    float4 o[MAXV];
+    float am = 0.f, nanck = 0.f;  // nanck: 0, or NaN if any value is NaN or infinite
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i < nv) {
+        const float4 ww = ld4(w + (lane + 64 * i) * 4);
+        o[i] = make_float4((v[i].x - mean) * inv * ww.x, (v[i].y - mean) * inv * ww.y, (v[i].z - mean) * inv * ww.z,
+                           (v[i].w - mean) * inv * ww.w);
+        am = fmaxf(am, fmaxf(fmaxf(fabsf(o[i].x), fabsf(o[i].y)), fmaxf(fabsf(o[i].z), fabsf(o[i].w))));
+        nanck += (o[i].x + o[i].y + o[i].z + o[i].w) * 0.f;
+      }
+    float sc, qi;
+    quant_params(wave_max(am) + wave_sum(nanck), sc, qi);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i < nv) *reinterpret_cast<uint32_t*>(hq + (lane + 64 * i) * 4) = quant4(o[i].x, o[i].y, o[i].z, o[i].w, qi);
+    if (lane == 0) *hs = sc;
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MAXV; ++i)
     if (i < nv) {
@@ -66,7 +89,8 @@ __global__ __launch_bounds__(256) void pre_norm_kernel(PreNormArgs a) {
 #pragma unroll
   for (int i = 0; i < MAXV; ++i)
     if (i < nv) v[i] = ld4(xr + (lane + 64 * i) * 4);
-  norm_write(v, nv, lane, a.D, a.kind, a.eps, a.w.v + a.row_sample[r] * a.w.stride, a.h + (int64_t)r * a.D);
+  norm_write(v, nv, lane, a.D, a.kind, a.eps, a.w.v + a.row_sample[r] * a.w.stride, a.h + (int64_t)r * a.D,
+             a.hq ? a.hq + (int64_t)r * a.D : nullptr, a.hq ? a.hs + r : nullptr);
 }
 
 // Both input rows (y bf16, x fp32) are requested before any arithmetic, so
@@ -109,7 +133,8 @@ __global__ __launch_bounds__(256) void post_norm_kernel(PostNormArgs a) {
       *reinterpret_cast<float4*>(xr + d) = v[i];
     }
   if (r >= a.n0 && r < a.n1)
-    norm_write(v, nv, lane, a.D, a.next_kind, a.next_eps, a.wn.v + sample * a.wn.stride, a.h + (int64_t)r * a.D);
+    norm_write(v, nv, lane, a.D, a.next_kind, a.next_eps, a.wn.v + sample * a.wn.stride, a.h + (int64_t)r * a.D,
+               a.hq ? a.hq + (int64_t)r * a.D : nullptr, a.hq ? a.hs + r : nullptr);
 }
 
 __global__ void fold_mod_kernel(const float* __restrict__ mod, int64_t mod_stride, const float* __restrict__ normw,
@@ -171,6 +196,67 @@ __global__ __launch_bounds__(256) void rows_rmsnorm_kernel(const void* x, const 
     }
 }
 
+// Per-row int8 quantization of bf16 or fp32 rows of width K (K % 8 == 0,
+// K <= 8 * 256 * QMAXC): one workgroup per row holds the row in registers
+// (16-byte chunks c = tid + 256 i), reduces max |v|, then writes 8 codes per
+// chunk and the row's scale.  Same arithmetic as the norm kernels' int8
+// output.
+constexpr int QMAXC = 8;
+template <bool BF16_IN>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
+                                                         int8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
+                                                         int K) {
+  __shared__ float red[8];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int nch = K >> 3;
+  float v[QMAXC][8];
+  float am = 0.f, nanck = 0.f;  // nanck: 0, or NaN if any value is NaN or infinite
+#pragma unroll
+  for (int i = 0; i < QMAXC; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      if constexpr (BF16_IN) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(x) + r * ldx + c * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[i][2 * k] = __uint_as_float(u[k] << 16);
+          v[i][2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+        }
+      } else {
+        const float* p = reinterpret_cast<const float*>(x) + r * ldx + c * 8;
+        const float4 a = ld4(p), b = ld4(p + 4);
+        v[i][0] = a.x, v[i][1] = a.y, v[i][2] = a.z, v[i][3] = a.w;
+        v[i][4] = b.x, v[i][5] = b.y, v[i][6] = b.z, v[i][7] = b.w;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        am = fmaxf(am, fabsf(v[i][k]));
+        nanck += v[i][k] * 0.f;
+      }
+    }
+  }
+  // fmaxf drops NaN operands, so the NaN check travels in a separate sum
+  am = wave_max(am);
+  nanck = wave_sum(nanck);
+  if ((tid & 63) == 0) {
+    red[tid >> 6] = am;
+    red[4 + (tid >> 6)] = nanck;
+  }
+  __syncthreads();
+  am = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) + (red[4] + red[5] + red[6] + red[7]);
+  float sc, qi;
+  quant_params(am, sc, qi);
+#pragma unroll
+  for (int i = 0; i < QMAXC; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      const u32x2 o = {quant4(v[i][0], v[i][1], v[i][2], v[i][3], qi), quant4(v[i][4], v[i][5], v[i][6], v[i][7], qi)};
+      *reinterpret_cast<u32x2*>(q + r * ldq + c * 8) = o;
+    }
+  }
+  if (tid == 0) s[r] = sc;
+}
+
 __global__ void patchify_kernel(const float* lat, bf16_t* out, int B, int C, int Hp, int Wp, int p,
                                 int npad) {
   const int64_t F = (int64_t)p * p * C;
@@ -200,6 +286,16 @@ hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s) {
   const int rows = a.r1 - a.r0;
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(post_norm_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* x, int x_bf16, int64_t ldx, int8_t* q, int64_t ldq, float* scale, int rows,
+                             int K, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (x_bf16)
+    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(rows), dim3(256), 0, s, x, ldx, q, ldq, scale, K);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(rows), dim3(256), 0, s, x, ldx, q, ldq, scale, K);
   return hipGetLastError();
 }
 

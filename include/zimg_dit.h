@@ -84,6 +84,16 @@ typedef struct zimg_dit_config {
                                 batch; 1: no such splits, so each sample's result is
                                 bitwise the same whatever else is in the batch (slower
                                 when the last round is partial) */
+  int32_t linear_int8;       /* 0 (default): bf16 block projections.  1: the seven
+                                projections of every block (to_q, to_k, to_v, to_out, w1,
+                                w2, w3) run on int8 codes with exact int32 sums: weights
+                                quantized per output row at finalize (symmetric, scale =
+                                max|w|/127), activations per token at run time (the same
+                                rule; see zimg_quantize_rows); embedders, conditioning,
+                                attention and the final layer stay as they are ("Z-Image-
+                                Turbo MNN (int8, fp16-safe)", Conversion details: 8-bit
+                                weights; "Z-Image" (AI Toolkit docs), Specifics: the
+                                embedders and final layer are not quantized) */
 } zimg_dit_config;
 
 /* One named weight tensor handed to the engine.  ``data`` is a HOST

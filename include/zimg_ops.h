@@ -59,6 +59,34 @@ int zimg_gemm_bf16(const void* A, int64_t lda, const void* W, int64_t ldw, void*
                    void* stream);
 
 /*
+ * Int8 projection GEMM: C = epilogue(dequant(A) dequant(W)^T) with the sums
+ * taken exactly in int32: C[m][n] = (float(sum_k A[m][k] W[n][k]) * sa[m]) *
+ * sw[n] (each product rounded to fp32), then the epilogue as for
+ * zimg_gemm_bf16 (ZIMG_EPI_BF16, ZIMG_EPI_F32_BIAS, ZIMG_EPI_SWIGLU).  The
+ * int8 block projections of "Z-Image-Turbo MNN (int8, fp16-safe)",
+ * Conversion details (8-bit weights), with activations quantized too.
+ * A DEVICE int8 [M, K] (row stride lda), W DEVICE int8 [N, K] (row stride
+ * ldw), sa DEVICE fp32 [M], sw DEVICE fp32 [N], C as for zimg_gemm_bf16.
+ * Constraints: K % 128 == 0, N % 256 == 0, lda, ldw multiples of 16, A and W
+ * 16-byte aligned.  ZIMG_EINVAL otherwise.
+ */
+int zimg_gemm_i8(const void* A, int64_t lda, const float* sa, const void* W, int64_t ldw, const float* sw, void* C,
+                 int64_t ldc, int32_t M, int32_t N, int32_t K, int32_t epilogue, const float* bias, void* stream);
+
+/*
+ * Symmetric per-row int8 quantization (the rule the int8 projections apply
+ * to weights and activations): for row r with amax = max_k |x[r][k]|,
+ * scale[r] = amax / 127 and inv = 127 / amax (each a correctly rounded fp32
+ * division), q[r][k] = rint(x[r][k] * inv) (fp32 product, ties to even)
+ * clamped to [-127, 127]; a row of zeros gets scale 0 and codes 0.
+ * x DEVICE [rows, K] fp32 or bf16 (x_dtype; row stride ldx, 16-byte
+ * aligned), q DEVICE int8 (row stride ldq, 8-byte aligned), scale DEVICE
+ * fp32 [rows].  K % 8 == 0, K <= 16384, ldx and ldq multiples of 8.
+ */
+int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
+                       int32_t rows, int32_t K, void* stream);
+
+/*
  * Euler update of the FlowMatch sampler: x[i] += dt * (-model_out[i]) for
  * i < n ("Z-Image-Turbo MNN (int8, fp16-safe)", Scheduler: the model output
  * is negated before the Euler step; dt = sigma'_{k+1} - sigma'_k).
@@ -92,7 +120,9 @@ int zimg_cfg_euler_step(float* x, const float* out_cond, const float* out_uncond
  * RoPE and the V transpose in its epilogue), gemm_out,
  * gemm_w13_swiglu, gemm_w2, attention, pre_norm, post_norm,
  * embed (patchify + caption norm + both embed GEMMs), final_layer,
- * conditioning (timestep MLP + the adaLN projection).
+ * conditioning (timestep MLP + the adaLN projection), quant (int8
+ * projections: the row quantization of the attention output and of the
+ * SwiGLU product).
  */
 typedef struct zimg_kernel_stat {
   const char* name; /* static string */

@@ -70,6 +70,7 @@ def test_full_manifest_counts():
     ("rope_axes", (32, 48, 40), "EUNSUPPORTED"),
     ("norm_eps", 0.0, "EINVAL"),
     ("batch_invariant", 2, "EINVAL"),
+    ("linear_int8", -1, "EINVAL"),
 ])
 def test_config_validation(field, value, code):
     b = _b()
