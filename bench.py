@@ -284,7 +284,8 @@ def int8_forward(args, wl, model, lat, caps, lens, t, n_img, tokens, bf16_ms):
     stats = dit.profile_read()
     dit.profile(False)
     dit.close()
-    kernels, roof, _ = summarize(stats, steps, work_per_forward(model, n_img, lens, int8=True), int8=True)
+    kernels, roof, dom = summarize(stats, steps, work_per_forward(model, n_img, lens, int8=True), int8=True)
+    roof["traffic"] = committed_traffic(f"{dom}_i8" if dom in INT8_CLASSES else dom, args.workload)
     ms = wall * 1e3 / steps
     log(f"int8 forward: {ms:.2f} ms")
     return {"workload": "the same forward with the 7 projections of every block on int8 codes "
