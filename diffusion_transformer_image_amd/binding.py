@@ -90,6 +90,8 @@ SIGNATURES = {
     "zimg_position_ids": (_I32, [_I32, _I32, _I32, _I32P, _I32P]),
     "zimg_rope_tables": (_I32, [ctypes.POINTER(Config), _I32P, _I64, _F32P, _F32P]),
     "zimg_row_layout": (_I32, [_I32, _I32, _I32P, _I32P, _I32P, _I32P]),
+    "zimg_row_layout_varsize": (_I32, [_I32, _I32P, _I32P, _I32P, _I32P, _I32P]),
+    "zimg_dit_forward_varsize": (_I32, [_P, _P, _I32, _I32P, _I32P, _P, _I32, _I32P, _F32P, _P, _P]),
     "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
     "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "zimg_gemm_i8": (_I32, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
@@ -238,6 +240,29 @@ class DiT:
                                       _stream(stream)), self._h)
         return out
 
+    def forward_varsize(self, latents, caption_feats, caption_lens, t, outs, stream=None):
+        """latents, outs: sequences of torch CUDA fp32 tensors [C, Hl_b, Wl_b]
+        (samples may differ in size); caption_feats packed as for forward."""
+        import torch
+        B = len(latents)
+        if len(outs) != B:
+            raise ValueError("one output per latent")
+        hl = np.ascontiguousarray([x.shape[-2] for x in latents], dtype=np.int32)
+        wl = np.ascontiguousarray([x.shape[-1] for x in latents], dtype=np.int32)
+        for x, o in zip(latents, outs):
+            if x.dtype != torch.float32 or o.dtype != torch.float32 or not x.is_contiguous() or not o.is_contiguous() \
+                    or tuple(o.shape[-3:]) != tuple(x.shape[-3:]):
+                raise ValueError("latents and outs: contiguous fp32 tensors of matching shapes")
+        lp = (ctypes.c_void_p * B)(*[x.data_ptr() for x in latents])
+        op = (ctypes.c_void_p * B)(*[o.data_ptr() for o in outs])
+        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
+        tt = np.ascontiguousarray(t, dtype=np.float32)
+        cap_dt = ZIMG_BF16 if caption_feats.dtype == torch.bfloat16 else ZIMG_F32
+        _check(lib().zimg_dit_forward_varsize(self._h, lp, B, hl.ctypes.data_as(_I32P), wl.ctypes.data_as(_I32P),
+                                              _ptr(caption_feats), cap_dt, lens.ctypes.data_as(_I32P),
+                                              tt.ctypes.data_as(_F32P), op, _stream(stream)), self._h)
+        return outs
+
     def run_blocks(self, x, B, Hl, Wl, caption_lens, t, first, n, stream=None):
         lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
         tt = np.ascontiguousarray(t, dtype=np.float32)
@@ -279,6 +304,18 @@ def row_layout(B, n_image_tokens, caption_lens):
     S = ctypes.c_int32()
     _check(lib().zimg_row_layout(B, n_image_tokens, lens.ctypes.data_as(_I32P), img.ctypes.data_as(_I32P),
                                  cap.ctypes.data_as(_I32P), ctypes.byref(S)))
+    return img, cap, S.value
+
+
+def row_layout_varsize(n_image_tokens, caption_lens):
+    n = np.ascontiguousarray(n_image_tokens, dtype=np.int32)
+    lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
+    B = len(n)
+    img = np.zeros(B, np.int32)
+    cap = np.zeros(B, np.int32)
+    S = ctypes.c_int32()
+    _check(lib().zimg_row_layout_varsize(B, n.ctypes.data_as(_I32P), lens.ctypes.data_as(_I32P),
+                                         img.ctypes.data_as(_I32P), cap.ctypes.data_as(_I32P), ctypes.byref(S)))
     return img, cap, S.value
 
 

@@ -239,32 +239,55 @@ void rope_rows(const double* omega, const int* axis, const int32_t* ids, int64_t
 
 // ------------------------------------------------------------------ layout
 
+// Rows of the batch: sample b's image tokens (N[b] = Hp[b] * Wp[b], padded
+// to Npad[b], a multiple of 16) from img_off[b], all samples' image rows
+// first, then each caption padded to a multiple of 16 from cap_off[b].
 struct Layout {
-  int B = 0, Hl = 0, Wl = 0, Hp = 0, Wp = 0, N = 0, Npad = 0;
-  std::vector<int> lens, img_off, cap_off;
+  int B = 0;
+  std::vector<int> Hl, Wl, Hp, Wp, N, Npad, lens, img_off, cap_off;
   int cap_base = 0, S = 0, Lsum = 0;
+  bool uniform = true;  // every sample has the same latent size
 };
 
-Layout make_layout(int B, int Hl, int Wl, int patch, const int32_t* lens) {
+Layout make_layout(int B, const int32_t* Hl, const int32_t* Wl, int patch, const int32_t* lens) {
   Layout L;
   L.B = B;
-  L.Hl = Hl;
-  L.Wl = Wl;
-  L.Hp = Hl / patch;
-  L.Wp = Wl / patch;
-  L.N = L.Hp * L.Wp;
-  L.Npad = (int)round_up(L.N, 16);
-  L.cap_base = B * L.Npad;
-  int off = L.cap_base;
+  int off = 0;
+  for (int b = 0; b < B; ++b) {
+    L.Hl.push_back(Hl[b]);
+    L.Wl.push_back(Wl[b]);
+    L.Hp.push_back(Hl[b] / patch);
+    L.Wp.push_back(Wl[b] / patch);
+    L.N.push_back(L.Hp[b] * L.Wp[b]);
+    L.Npad.push_back((int)round_up(L.N[b], 16));
+    L.img_off.push_back(off);
+    off += L.Npad[b];
+    L.uniform = L.uniform && Hl[b] == Hl[0] && Wl[b] == Wl[0];
+  }
+  L.cap_base = off;
   for (int b = 0; b < B; ++b) {
     L.lens.push_back(lens[b]);
-    L.img_off.push_back(b * L.Npad);
     L.cap_off.push_back(off);
     off += (int)round_up(lens[b], 16);
     L.Lsum += lens[b];
   }
   L.S = off;
   return L;
+}
+
+Layout make_layout(int B, int Hl, int Wl, int patch, const int32_t* lens) {
+  std::vector<int32_t> hv(B, Hl), wv(B, Wl);
+  return make_layout(B, hv.data(), wv.data(), patch, lens);
+}
+
+// True when the B per-sample buffers of a one-size batch are consecutive
+// slices of one [B, C, Hl, Wl] array.
+template <class T>
+bool contiguous(T* const* p, const Layout& L, int C) {
+  const int64_t n = (int64_t)C * L.Hl[0] * L.Wl[0];
+  for (int b = 1; b < L.B; ++b)
+    if (p[b] != p[0] + b * n) return false;
+  return true;
 }
 
 }  // namespace
@@ -425,8 +448,8 @@ struct zimg_dit {
   int finalize();
   int prepare(const Layout& L, const float* t, hipStream_t s);
   int run_block(int bi, const Layout& L, bool h_ready, int next, hipStream_t s);
-  int forward(const float* latent, const Layout& L, const void* caps, int cap_dtype, const float* t, float* out,
-              hipStream_t s);
+  int forward(const float* const* latents, const Layout& L, const void* caps, int cap_dtype, const float* t,
+              float* const* outs, hipStream_t s);
   int run_blocks(float* x_io, const Layout& L, const float* t, int first, int n, hipStream_t s);
 };
 
@@ -658,8 +681,12 @@ int zimg_dit::finalize() {
 // block's modulation.
 int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
   const zimg_dit_config& c = cfg;
-  std::vector<int32_t> key = {L.B, L.Hl, L.Wl};
-  for (int v : L.lens) key.push_back(v);
+  std::vector<int32_t> key = {L.B};
+  for (int b = 0; b < L.B; ++b) {
+    key.push_back(L.Hl[b]);
+    key.push_back(L.Wl[b]);
+    key.push_back(L.lens[b]);
+  }
   if (key != table_key) {
     HIP_TRY(hipEventSynchronize(staging_done));  // previous upload has left the staging buffer
     char* st = (char*)staging;
@@ -676,13 +703,14 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
     double omega[64];
     int axis[64];
     rope_freqs(c, omega, axis);
-    std::vector<int32_t> cap_ids, img_ids((size_t)L.N * 3);
+    std::vector<int32_t> cap_ids, img_ids;
     for (int b = 0; b < L.B; ++b) {
       cap_ids.assign((size_t)L.lens[b] * 3, 0);
-      position_ids(L.lens[b], L.Hp, L.Wp, cap_ids.data(), img_ids.data());
-      rope_rows(omega, axis, img_ids.data(), L.N, cs + (int64_t)L.img_off[b] * 64, sn + (int64_t)L.img_off[b] * 64);
+      img_ids.assign((size_t)L.N[b] * 3, 0);
+      position_ids(L.lens[b], L.Hp[b], L.Wp[b], cap_ids.data(), img_ids.data());
+      rope_rows(omega, axis, img_ids.data(), L.N[b], cs + (int64_t)L.img_off[b] * 64, sn + (int64_t)L.img_off[b] * 64);
       rope_rows(omega, axis, cap_ids.data(), L.lens[b], cs + (int64_t)L.cap_off[b] * 64, sn + (int64_t)L.cap_off[b] * 64);
-      for (int i = 0; i < L.Npad; ++i) rs[L.img_off[b] + i] = b;
+      for (int i = 0; i < L.Npad[b]; ++i) rs[L.img_off[b] + i] = b;
       for (int i = 0; i < (int)round_up(L.lens[b], 16); ++i) rs[L.cap_off[b] + i] = b;
     }
     // segments and q-tiles of 128 rows per stage
@@ -694,7 +722,7 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
         int k = 0;
         if (stg != 1) {
           q.r0[k] = L.img_off[b];
-          q.n[k++] = L.N;
+          q.n[k++] = L.N[b];
         }
         if (stg != 0) {
           q.r0[k] = L.cap_off[b];
@@ -895,22 +923,29 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   return ZIMG_OK;
 }
 
-int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, int cap_dtype, const float* t,
-                      float* out, hipStream_t s) {
+int zimg_dit::forward(const float* const* latents, const Layout& L, const void* caps, int cap_dtype, const float* t,
+                      float* const* outs, hipStream_t s) {
   const zimg_dit_config& c = cfg;
   const int D = c.hidden, P = c.patch * c.patch * c.in_channels;
   int rc = prepare(L, t, s);
   if (rc) return rc;
-  // patch embed -> image rows of x (fp32, bias); caption embed -> caption rows
+  // patch embed -> image rows of x (fp32, bias); caption embed -> caption rows.
+  // A batch of one latent size (contiguous latents) is patchified in one
+  // launch; otherwise sample by sample.
   rc = prof_start(K_EMBED, s);
   if (rc) return rc;
-  HIP_TRY(zimg::launch_patchify(latent, xin, L.B, c.in_channels, L.Hp, L.Wp, c.patch, L.Npad, s));
+  if (L.uniform && contiguous(latents, L, c.in_channels))
+    HIP_TRY(zimg::launch_patchify(latents[0], xin, L.B, c.in_channels, L.Hp[0], L.Wp[0], c.patch, L.Npad[0], s));
+  else
+    for (int b = 0; b < L.B; ++b)
+      HIP_TRY(zimg::launch_patchify(latents[b], xin + (int64_t)L.img_off[b] * P, 1, c.in_channels, L.Hp[b], L.Wp[b],
+                                    c.patch, L.Npad[b], s));
   zimg::GemmArgs ga{};
   ga.A = xin;
   ga.lda = P;
   ga.W = x_w;
   ga.ldw = P;
-  ga.M = L.B * L.Npad;
+  ga.M = L.cap_base;
   ga.N = D;
   ga.K = P;
   ga.epi = zimg::EPI_F32_BIAS;
@@ -964,27 +999,35 @@ int zimg_dit::forward(const float* latent, const Layout& L, const void* caps, in
                          L.cap_base, D, c.final_eps, 1};
     HIP_TRY(zimg::launch_pre_norm(pa, s));
   }
-  // final linear + unpatchify
-  ga = zimg::GemmArgs{};
-  ga.A = h;
-  ga.lda = D;
-  ga.W = fin_w;
-  ga.ldw = D;
-  ga.M = L.cap_base;
-  ga.N = P;
-  ga.K = D;
-  ga.epi = zimg::EPI_UNPATCH;
-  ga.role = zimg::ROLE_FINAL;
-  ga.split = gemm_split();
-  ga.ep.C = out;
-  ga.ep.bias = fin_b;
-  ga.ep.ntok = L.N;
-  ga.ep.npad = L.Npad;
-  ga.ep.Hp = L.Hp;
-  ga.ep.Wp = L.Wp;
-  ga.ep.C_ch = c.in_channels;
-  ga.ep.patch = c.patch;
-  HIP_TRY(zimg::launch_gemm(ga, s));
+  // final linear + unpatchify: one launch for a batch of one latent size
+  // (contiguous outputs), else one per sample
+  auto final_gemm = [&](int r0, int rows, int b0, float* dst) -> hipError_t {
+    zimg::GemmArgs gf{};
+    gf.A = h + (int64_t)r0 * D;
+    gf.lda = D;
+    gf.W = fin_w;
+    gf.ldw = D;
+    gf.M = rows;
+    gf.N = P;
+    gf.K = D;
+    gf.epi = zimg::EPI_UNPATCH;
+    gf.role = zimg::ROLE_FINAL;
+    gf.split = gemm_split();
+    gf.ep.C = dst;
+    gf.ep.bias = fin_b;
+    gf.ep.ntok = L.N[b0];
+    gf.ep.npad = L.Npad[b0];
+    gf.ep.Hp = L.Hp[b0];
+    gf.ep.Wp = L.Wp[b0];
+    gf.ep.C_ch = c.in_channels;
+    gf.ep.patch = c.patch;
+    return zimg::launch_gemm(gf, s);
+  };
+  if (L.uniform && contiguous(outs, L, c.in_channels)) {
+    HIP_TRY(final_gemm(0, L.cap_base, 0, outs[0]));
+  } else {
+    for (int b = 0; b < L.B; ++b) HIP_TRY(final_gemm(L.img_off[b], L.Npad[b], b, outs[b]));
+  }
   return prof_stop(s);
 }
 
@@ -1008,16 +1051,21 @@ int zimg_dit::run_blocks(float* x_io, const Layout& L, const float* t, int first
 
 namespace {
 
-int validate_inputs(const zimg_dit* h, int32_t B, int32_t Hl, int32_t Wl, const int32_t* lens, const float* t) {
+int validate_inputs(const zimg_dit* h, int32_t B, const int32_t* Hl, const int32_t* Wl, const int32_t* lens,
+                    const float* t) {
   const zimg_dit_config& c = h->cfg;
   if (!h->finalized) return set_err(ZIMG_ESTATE, "weights not finalized (missing zimg_dit_finalize?)");
   if (B < 1 || B > c.max_batch) return set_err(ZIMG_EINVAL, "batch %d out of range 1..%d", B, c.max_batch);
-  if (Hl <= 0 || Wl <= 0 || Hl % c.patch || Wl % c.patch)
-    return set_err(ZIMG_EINVAL, "latent %dx%d: sides must be positive multiples of the patch size %d (image sides multiples of 16)",
-                   Hl, Wl, c.patch);
-  const int64_t ntok = (int64_t)(Hl / c.patch) * (Wl / c.patch);
-  if (ntok > c.max_image_tokens)
-    return set_err(ZIMG_EINVAL, "%lld image tokens exceed max_image_tokens %d", (long long)ntok, c.max_image_tokens);
+  if (!Hl || !Wl) return set_err(ZIMG_EINVAL, "latent sizes must be host arrays, got NULL");
+  for (int b = 0; b < B; ++b) {
+    if (Hl[b] <= 0 || Wl[b] <= 0 || Hl[b] % c.patch || Wl[b] % c.patch)
+      return set_err(ZIMG_EINVAL,
+                     "latent %dx%d: sides must be positive multiples of the patch size %d (image sides multiples of 16)",
+                     Hl[b], Wl[b], c.patch);
+    const int64_t ntok = (int64_t)(Hl[b] / c.patch) * (Wl[b] / c.patch);
+    if (ntok > c.max_image_tokens)
+      return set_err(ZIMG_EINVAL, "%lld image tokens exceed max_image_tokens %d", (long long)ntok, c.max_image_tokens);
+  }
   if (!lens || !t) return set_err(ZIMG_EINVAL, "caption_lens and t must be host arrays, got NULL");
   for (int b = 0; b < B; ++b) {
     if (lens[b] < 1 || lens[b] > c.max_caption_tokens)
@@ -1025,6 +1073,28 @@ int validate_inputs(const zimg_dit* h, int32_t B, int32_t Hl, int32_t Wl, const 
     if (!std::isfinite(t[b])) return set_err(ZIMG_EINVAL, "t[%d] is not finite", b);
   }
   return ZIMG_OK;
+}
+
+int validate_inputs(const zimg_dit* h, int32_t B, int32_t Hl, int32_t Wl, const int32_t* lens, const float* t) {
+  if (B < 1 || B > 4096) return set_err(ZIMG_EINVAL, "batch %d out of range 1..%d", B, h->cfg.max_batch);
+  std::vector<int32_t> hv(B, Hl), wv(B, Wl);
+  return validate_inputs(h, B, hv.data(), wv.data(), lens, t);
+}
+
+// Forward on per-sample latent / output buffers (validated arguments).
+int run_forward(zimg_dit* h, const float* const* latents, int32_t B, const int32_t* Hl, const int32_t* Wl,
+                const void* caption_feats, int32_t cap_dtype, const int32_t* caption_lens, const float* t,
+                float* const* outs, void* stream) {
+  if (!caption_feats) return set_err(ZIMG_EINVAL, "caption_feats must be non-NULL");
+  for (int b = 0; b < B; ++b)
+    if (!latents[b] || !outs[b]) return set_err(ZIMG_EINVAL, "latent and output buffers must be non-NULL");
+  if (cap_dtype != ZIMG_F32 && cap_dtype != ZIMG_BF16) return set_err(ZIMG_EINVAL, "cap_dtype must be ZIMG_F32 or ZIMG_BF16");
+  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
+  if (h->cap_buf) {
+    const size_t need = (size_t)(h->blocks.size() + 1) * L.S * h->cfg.hidden * 4;
+    if (h->cap_bytes < need) return set_err(ZIMG_EINVAL, "capture buffer has %zu bytes, needs %zu", h->cap_bytes, need);
+  }
+  return h->forward(latents, L, caption_feats, cap_dtype, t, outs, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -1152,14 +1222,28 @@ int zimg_dit_forward(zimg_dit* h, const float* latent, int32_t B, int32_t Hl, in
   if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
   int rc = validate_inputs(h, B, Hl, Wl, caption_lens, t);
   if (rc) return h->fail(rc);
-  if (!latent || !caption_feats || !out) return h->fail(set_err(ZIMG_EINVAL, "latent, caption_feats and out must be non-NULL"));
-  if (cap_dtype != ZIMG_F32 && cap_dtype != ZIMG_BF16) return h->fail(set_err(ZIMG_EINVAL, "cap_dtype must be ZIMG_F32 or ZIMG_BF16"));
-  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
-  if (h->cap_buf) {
-    const size_t need = (size_t)(h->blocks.size() + 1) * L.S * h->cfg.hidden * 4;
-    if (h->cap_bytes < need) return h->fail(set_err(ZIMG_EINVAL, "capture buffer has %zu bytes, needs %zu", h->cap_bytes, need));
+  if (!latent || !out) return h->fail(set_err(ZIMG_EINVAL, "latent, caption_feats and out must be non-NULL"));
+  const int64_t n = (int64_t)h->cfg.in_channels * Hl * Wl;
+  std::vector<const float*> lat(B);
+  std::vector<float*> outs(B);
+  std::vector<int32_t> hv(B, Hl), wv(B, Wl);
+  for (int b = 0; b < B; ++b) {
+    lat[b] = latent + b * n;
+    outs[b] = out + b * n;
   }
-  rc = h->forward(latent, L, caption_feats, cap_dtype, t, out, (hipStream_t)stream);
+  rc = run_forward(h, lat.data(), B, hv.data(), wv.data(), caption_feats, cap_dtype, caption_lens, t, outs.data(), stream);
+  return rc ? h->fail(rc) : ZIMG_OK;
+}
+
+int zimg_dit_forward_varsize(zimg_dit* h, const float* const* latents, int32_t B, const int32_t* Hl, const int32_t* Wl,
+                             const void* caption_feats, int32_t cap_dtype, const int32_t* caption_lens, const float* t,
+                             float* const* outs, void* stream) {
+  g_last_error.clear();
+  if (!h) return set_err(ZIMG_EINVAL, "handle is NULL");
+  if (!latents || !outs) return h->fail(set_err(ZIMG_EINVAL, "latents and outs must be host arrays, got NULL"));
+  int rc = validate_inputs(h, B, Hl, Wl, caption_lens, t);
+  if (rc) return h->fail(rc);
+  rc = run_forward(h, latents, B, Hl, Wl, caption_feats, cap_dtype, caption_lens, t, outs, stream);
   return rc ? h->fail(rc) : ZIMG_OK;
 }
 
@@ -1178,21 +1262,30 @@ int zimg_dit_run_blocks(zimg_dit* h, float* x_io, int32_t B, int32_t Hl, int32_t
   return rc ? h->fail(rc) : ZIMG_OK;
 }
 
-int zimg_row_layout(int32_t B, int32_t n_image_tokens, const int32_t* caption_lens, int32_t* img_off, int32_t* cap_off,
-                    int32_t* S_total) {
+int zimg_row_layout_varsize(int32_t B, const int32_t* n_image_tokens, const int32_t* caption_lens, int32_t* img_off,
+                            int32_t* cap_off, int32_t* S_total) {
   g_last_error.clear();
-  if (B < 1 || n_image_tokens < 1 || !caption_lens) return set_err(ZIMG_EINVAL, "bad layout arguments");
+  if (B < 1 || !n_image_tokens || !caption_lens) return set_err(ZIMG_EINVAL, "bad layout arguments");
   for (int b = 0; b < B; ++b)
-    if (caption_lens[b] < 1) return set_err(ZIMG_EINVAL, "caption length must be >= 1");
-  const int64_t npad = round_up(n_image_tokens, 16);
-  int64_t off = (int64_t)B * npad;
+    if (caption_lens[b] < 1 || n_image_tokens[b] < 1) return set_err(ZIMG_EINVAL, "token counts must be >= 1");
+  int64_t off = 0;
   for (int b = 0; b < B; ++b) {
-    if (img_off) img_off[b] = (int32_t)(b * npad);
+    if (img_off) img_off[b] = (int32_t)off;
+    off += round_up(n_image_tokens[b], 16);
+  }
+  for (int b = 0; b < B; ++b) {
     if (cap_off) cap_off[b] = (int32_t)off;
     off += round_up(caption_lens[b], 16);
   }
   if (S_total) *S_total = (int32_t)off;
   return ZIMG_OK;
+}
+
+int zimg_row_layout(int32_t B, int32_t n_image_tokens, const int32_t* caption_lens, int32_t* img_off, int32_t* cap_off,
+                    int32_t* S_total) {
+  if (B < 1) return set_err(ZIMG_EINVAL, "bad layout arguments");
+  std::vector<int32_t> n(B, n_image_tokens);
+  return zimg_row_layout_varsize(B, n.data(), caption_lens, img_off, cap_off, S_total);
 }
 
 int zimg_position_ids(int32_t L, int32_t Hp, int32_t Wp, int32_t* cap_ids, int32_t* img_ids) {

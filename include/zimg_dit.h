@@ -167,6 +167,24 @@ int zimg_dit_forward(zimg_dit* h, const float* latent, int32_t B, int32_t Hl, in
                      const int32_t* caption_lens, const float* t, float* out,
                      void* stream);
 
+/*
+ * One forward over a batch whose samples may differ in image size as well as
+ * caption length ("Local component coverage and quality handoff for the
+ * zimage FastVideo port", Transformer: parity on variable-length image/text
+ * batches; the padded variable-length stream needs a key mask).  Each
+ * sample's image and caption tokens form its own sequence; no token attends
+ * across samples, so every sample's output equals that sample run alone.
+ *   latents   HOST array [B] of DEVICE pointers, latent b fp32
+ *             [in_channels, Hl[b], Wl[b]]
+ *   Hl, Wl    HOST int32 [B], each even; (Hl[b]/2)*(Wl[b]/2) <= max_image_tokens
+ *   outs      HOST array [B] of DEVICE pointers, output b fp32 of latent b's shape
+ * Other arguments and errors as for zimg_dit_forward (which is this call for
+ * B latents of one size stored back to back).
+ */
+int zimg_dit_forward_varsize(zimg_dit* h, const float* const* latents, int32_t B, const int32_t* Hl,
+                             const int32_t* Wl, const void* caption_feats, int32_t cap_dtype,
+                             const int32_t* caption_lens, const float* t, float* const* outs, void* stream);
+
 /* Release all device and host memory of the handle (NULL is a no-op). */
 void zimg_dit_destroy(zimg_dit* h);
 

@@ -28,6 +28,13 @@ extern "C" {
 int zimg_row_layout(int32_t B, int32_t n_image_tokens, const int32_t* caption_lens,
                     int32_t* img_off, int32_t* cap_off, int32_t* S_total);
 
+/* The same layout for samples with their own image token counts (HOST
+ * n_image_tokens [B]): sample b's image rows start at img_off[b], the sum of
+ * the earlier samples' counts each rounded up to 16 (the layout of
+ * zimg_dit_forward_varsize). */
+int zimg_row_layout_varsize(int32_t B, const int32_t* n_image_tokens, const int32_t* caption_lens,
+                            int32_t* img_off, int32_t* cap_off, int32_t* S_total);
+
 /*
  * Run blocks [first_block, first_block + n_blocks) of the model (execution
  * order: noise refiners, context refiners, joint blocks) in place on the

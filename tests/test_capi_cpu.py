@@ -131,6 +131,20 @@ def test_row_layout():
         _b().row_layout(1, 16, [0])
 
 
+def test_row_layout_varsize():
+    """Per-sample image counts: 120 -> 128 rows, 6 -> 16, 17 -> 32 (image rows
+    of all samples first), then captions 77 -> 80, 1 -> 16, 33 -> 48."""
+    img, cap, S = _b().row_layout_varsize([120, 6, 17], [77, 1, 33])
+    assert img.tolist() == [0, 128, 144]
+    assert cap.tolist() == [176, 256, 272] and S == 320
+    # equal counts give the uniform layout
+    for n, lens in ((3840, [77, 300]), (600, [1, 16, 17])):
+        assert [a.tolist() if hasattr(a, "tolist") else a for a in _b().row_layout_varsize([n] * len(lens), lens)] == \
+            [a.tolist() if hasattr(a, "tolist") else a for a in _b().row_layout(len(lens), n, lens)]
+    with pytest.raises(_b().ZimgError):
+        _b().row_layout_varsize([16, 0], [1, 1])
+
+
 def test_sampler_schedule_equals_oracle():
     from diffusion_transformer_image_amd import sampler
     for n, s in [(8, 3.0), (28, 6.0), (1, 3.0)]:
