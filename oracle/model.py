@@ -226,25 +226,27 @@ def attention(q, k, v, q_chunk=2048):
     return out
 
 
-def linear(x, w, quant=None, held="f32"):
+def linear(x, w, quant=None, held="f32", rotate=False):
     """x W^T without bias.  quant None: float64.  quant "int8": the W8A8
     product of oracle.quant, with x quantized from the precision it is held
-    in when it reaches the projection (``held``: "f32" or "bf16")."""
+    in when it reaches the projection (``held``: "f32" or "bf16"), rotated
+    first when ``rotate`` (w2's input)."""
     if quant is None:
         return _f64(x) @ _f64(w).T
     if quant != "int8":
         raise ValueError(f"unknown quantization {quant!r}")
     xh = qz.to_bf16(x) if held == "bf16" else qz.to_f32(x)
-    return qz.int8_linear(xh, w)
+    return qz.int8_linear(xh, w, rotate=rotate)
 
 
 def swiglu_ffn(W, prefix, h, quant=None):
     """w2( SiLU(w1 h) * (w3 h) ), no biases ([AIT] "Architecture": SwiGLU
     FFN; [MNN] "Conversion details": weights w1, w2, w3).  With int8
-    projections, the SwiGLU product reaches w2 as bf16 values."""
+    projections, the SwiGLU product reaches w2 as bf16 values and is rotated
+    before it is quantized (oracle.quant)."""
     a = linear(h, W[f"{prefix}.feed_forward.w1.weight"], quant)
     b = linear(h, W[f"{prefix}.feed_forward.w3.weight"], quant)
-    return linear(silu(a) * b, W[f"{prefix}.feed_forward.w2.weight"], quant, held="bf16")
+    return linear(silu(a) * b, W[f"{prefix}.feed_forward.w2.weight"], quant, held="bf16", rotate=True)
 
 
 def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=None, quant=None):

@@ -24,7 +24,17 @@ int8 so that the product runs on integer matrix units):
   * weights are quantized from their bf16 values; the normalised block
     inputs h and h2 from their fp32 values; the attention output and the
     SwiGLU product from their bf16 values (the precision each is held in
-    when it reaches the projection).
+    when it reaches the projection);
+  * the SwiGLU product (w2's input) is heavy-tailed, so before it is
+    quantized it is rotated, as the ConvRot quantization of [H3D] ("What was
+    changed, and why": ConvRot rotates the activation) rotates activations:
+    every 128 consecutive values of a row go through the unnormalised
+    Walsh-Hadamard transform (the Sylvester matrix H_128, H H^T = 128 I), and
+    w2's weight rows through the same transform, so the product of the two
+    rotated operands is 128 times the plain one; the rotated weights'
+    scales carry the 1/128 (an exact power of two).  The transform is the
+    fast one in fp32: butterflies of stride 1, 2, 4, ..., 64 in that order,
+    (a, b) -> (a + b, a - b).
 The block's adaLN linears and the attention itself stay in floating point.
 """
 
@@ -61,6 +71,46 @@ def quantize_rows(x):
     return codes, scale
 
 
+def sylvester_hadamard(n):
+    """H_1 = [1]; H_2m = [[H_m, H_m], [H_m, -H_m]] (float64)."""
+    H = np.ones((1, 1))
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    assert H.shape[0] == n
+    return H
+
+
+ROT_BLOCK = 128
+
+
+def fwht_rows(x, n=ROT_BLOCK):
+    """Fast Walsh-Hadamard transform of every n consecutive values of each
+    row, in fp32: for stride h = 1, 2, ..., n/2, each pair (i, i + h) with
+    bit h of i clear becomes (x_i + x_{i+h}, x_i - x_{i+h}), rounded to fp32.
+    Equals x times the Sylvester matrix H_n on each block, up to rounding."""
+    v = to_f32(x).copy()
+    shape = v.shape
+    v = v.reshape(-1, n)
+    h = 1
+    while h < n:
+        b = v.reshape(-1, n // (2 * h), 2, h)
+        lo, hi = b[:, :, 0, :].copy(), b[:, :, 1, :].copy()
+        b[:, :, 0, :] = (lo + hi).astype(np.float32)
+        b[:, :, 1, :] = (lo - hi).astype(np.float32)
+        v = b.reshape(-1, n)
+        h *= 2
+    return v.reshape(shape)
+
+
+def quantize_rotated_rows(x, weight=False):
+    """Codes and scales of the rotated rows (the SwiGLU product, held as
+    bf16, or w2's weight rows); the weight scales carry the 1/128."""
+    q, s = quantize_rows(fwht_rows(x))
+    if weight:
+        s = (s * np.float32(1.0 / ROT_BLOCK)).astype(np.float32)
+    return q, s
+
+
 def int_matmul(qa, qw):
     """acc[i, j] = sum_k qa[i, k] * qw[j, k], exactly.  Computed as a
     float64 matrix product: each term is an integer of magnitude at most
@@ -80,9 +130,14 @@ def int8_product(qa, sa, qw, sw):
     return acc * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
 
 
-def int8_linear(x, w):
+def int8_linear(x, w, rotate=False):
     """x [M, K] (values as held: fp32 or bf16) times W^T, W [N, K] (bf16
-    values), both quantized per row."""
-    qa, sa = quantize_rows(x)
-    qw, sw = quantize_rows(w)
+    values), both quantized per row; with ``rotate`` both are first rotated
+    by blocks of 128 (see the module docstring)."""
+    if rotate:
+        qa, sa = quantize_rotated_rows(x)
+        qw, sw = quantize_rotated_rows(w, weight=True)
+    else:
+        qa, sa = quantize_rows(x)
+        qw, sw = quantize_rows(w)
     return int8_product(qa, sa, qw, sw)

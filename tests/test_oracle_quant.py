@@ -121,3 +121,45 @@ def test_int8_forward_near_float_forward_tiny():
     r = helpers.rel_l2(got, ref)
     assert 1e-5 < r < 2e-2, r
     assert helpers.cosine(got, ref) > 0.9996
+
+
+def test_sylvester_hadamard_closed_form():
+    """H_n[i, j] = (-1)^popcount(i & j); H H^T = n I."""
+    for n in (1, 2, 8, 128):
+        H = qz.sylvester_hadamard(n)
+        want = np.array([[(-1) ** bin(i & j).count("1") for j in range(n)] for i in range(n)], np.float64)
+        assert np.array_equal(H, want)
+        assert np.array_equal(H @ H.T, n * np.eye(n))
+
+
+def test_fwht_equals_matrix_product():
+    """On small integers every butterfly is exact in fp32, so the fast
+    transform equals the block-wise product with H_128 exactly; on random
+    values, to fp32 rounding."""
+    rng = np.random.default_rng(8)
+    H = qz.sylvester_hadamard(128)
+    xi = rng.integers(-1000, 1001, (3, 384)).astype(np.float32)
+    want = (xi.astype(np.float64).reshape(3, 3, 128) @ H).reshape(3, 384)
+    assert np.array_equal(qz.fwht_rows(xi).astype(np.float64), want)
+    xr = rng.standard_normal((4, 256)).astype(np.float32)
+    want = (xr.astype(np.float64).reshape(4, 2, 128) @ H).reshape(4, 256)
+    assert np.allclose(qz.fwht_rows(xr), want, rtol=0, atol=1e-5 * np.abs(xr).max() * 128)
+
+
+def test_rotation_cancels_in_the_product():
+    """(x H)(w H)^T = 128 x w^T, so the rotated int8 product estimates the
+    same x w^T; for a heavy-tailed x (a product of two normals, like the
+    SwiGLU product) it does so with a smaller error than without rotation."""
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((16, 1024)) * rng.standard_normal((16, 1024))).astype(np.float32)
+    w = synthetic.bf16_round(rng.standard_normal((32, 1024)).astype(np.float32) * 0.02)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    rot = qz.fwht_rows(x).astype(np.float64) @ qz.fwht_rows(w).astype(np.float64).T / 128
+    assert np.allclose(rot, ref, rtol=0, atol=1e-4 * np.abs(ref).max())
+    e_rot = helpers.rel_l2(qz.int8_linear(x, w, rotate=True), ref)
+    e_plain = helpers.rel_l2(qz.int8_linear(x, w), ref)
+    assert e_rot < 0.75 * e_plain, (e_rot, e_plain)
+    # the weight scales carry the exact 1/128
+    _, s = qz.quantize_rows(qz.fwht_rows(w))
+    _, sr = qz.quantize_rotated_rows(w, weight=True)
+    assert np.array_equal(sr * np.float32(128), s)
