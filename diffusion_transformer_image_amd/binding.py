@@ -95,7 +95,7 @@ SIGNATURES = {
     "zimg_dit_run_blocks": (_I32, [_P, _P, _I32, _I32, _I32, _I32P, _F32P, _I32, _I32, _P]),
     "zimg_gemm_bf16": (_I32, [_P, _I64, _P, _I64, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "zimg_gemm_i8": (_I32, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
-    "zimg_quantize_rows": (_I32, [_P, _I32, _I64, _P, _I64, _P, _I32, _I32, _P]),
+    "zimg_quantize_rows": (_I32, [_P, _I32, _I64, _P, _I64, _P, _I32, _I32, _I32, _P]),
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
     "zimg_cfg_euler_step": (_I32, [_P, _P, _P, ctypes.c_float, ctypes.c_float, _I64, _P]),
     "zimg_dit_profile": (_I32, [_P, _I32]),
@@ -355,15 +355,16 @@ def gemm_i8(A, sa, W, sw, C, epilogue=EPI_BF16, bias=None, stream=None):
     return C
 
 
-def quantize_rows(x, q, scale, stream=None):
-    """Per-row int8 codes q and scales of x (torch CUDA fp32 or bf16 rows)."""
+def quantize_rows(x, q, scale, rotate_block=0, stream=None):
+    """Per-row int8 codes q and scales of x (torch CUDA fp32 or bf16 rows),
+    after a 128-point Walsh-Hadamard rotation when rotate_block is 128."""
     import torch
     rows, K = x.shape
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"quantize_rows takes fp32 or bf16 rows, got {x.dtype}")
     dt = ZIMG_BF16 if x.dtype == torch.bfloat16 else ZIMG_F32
     _check(lib().zimg_quantize_rows(_ptr(x), dt, x.stride(0), _ptr(q), q.stride(0), _ptr(scale), rows, K,
-                                    _stream(stream)))
+                                    rotate_block, _stream(stream)))
     return q, scale
 
 

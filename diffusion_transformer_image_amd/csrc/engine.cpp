@@ -659,10 +659,12 @@ int zimg_dit::finalize() {
     // quantize every block projection per output row, then drop the bf16 copies
     const int D = cfg.hidden, F = cfg.ffn;
     for (BlockW& w : bw) {
-      HIP_TRY(zimg::launch_quant_rows(w.wqkv, 1, D, w.qqkv, D, w.sqkv, 3 * D, D, nullptr));
-      HIP_TRY(zimg::launch_quant_rows(w.wo, 1, D, w.qo, D, w.so, D, D, nullptr));
-      HIP_TRY(zimg::launch_quant_rows(w.w13, 1, D, w.q13, D, w.s13, 2 * F, D, nullptr));
-      HIP_TRY(zimg::launch_quant_rows(w.w2, 1, F, w.q2, F, w.s2, D, F, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.wqkv, 1, D, w.qqkv, D, w.sqkv, 3 * D, D, 0, 1.0f, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.wo, 1, D, w.qo, D, w.so, D, D, 0, 1.0f, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.w13, 1, D, w.q13, D, w.s13, 2 * F, D, 0, 1.0f, nullptr));
+      // w2's input is rotated by 128-point Walsh-Hadamard blocks at run time;
+      // its weight rows get the same transform, and their scales the 1/128
+      HIP_TRY(zimg::launch_quant_rows(w.w2, 1, F, w.q2, F, w.s2, D, F, 1, 1.0f / 128.0f, nullptr));
     }
     HIP_TRY(hipDeviceSynchronize());
     for (BlockW& w : bw) {
@@ -855,7 +857,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
                     split.ws};
   PROFILED(K_ATTN, zimg::launch_attention(aa, s));
 
-  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(o + (int64_t)r0 * D, 1, D, oq + (int64_t)r0 * D, D, os + r0, M, D, s));
+  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(o + (int64_t)r0 * D, 1, D, oq + (int64_t)r0 * D, D, os + r0, M, D, 0, 1.0f, s));
   operands(o, oq, os, w.wo, w.qo, w.so, D);
   ga.N = D;
   ga.ep.C = y + (int64_t)r0 * D;
@@ -892,7 +894,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
   ga.split = gemm_split();
   PROFILED(K_W13, zimg::launch_gemm(ga, s));
 
-  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(g + (int64_t)r0 * F, 1, F, gq + (int64_t)r0 * F, F, gs + r0, M, F, s));
+  if (i8) PROFILED(K_QUANT, zimg::launch_quant_rows(g + (int64_t)r0 * F, 1, F, gq + (int64_t)r0 * F, F, gs + r0, M, F, 1, 1.0f, s));
   operands(g, gq, gs, w.w2, w.q2, w.s2, F);
   ga.N = D;
   ga.K = F;
@@ -1363,7 +1365,7 @@ int zimg_gemm_i8(const void* A, int64_t lda, const float* sa, const void* W, int
 }
 
 int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
-                       int32_t rows, int32_t K, void* stream) {
+                       int32_t rows, int32_t K, int32_t rotate_block, void* stream) {
   g_last_error.clear();
   if (rows < 0 || K <= 0 || K % 8 || K > 16384) return set_err(ZIMG_EINVAL, "need rows >= 0 and K a multiple of 8 in 8..16384");
   if (x_dtype != ZIMG_F32 && x_dtype != ZIMG_BF16) return set_err(ZIMG_EINVAL, "unknown dtype %d", x_dtype);
@@ -1371,7 +1373,10 @@ int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, i
   if (rows > 0 && (!x || !q || !scale)) return set_err(ZIMG_EINVAL, "NULL buffer");
   const uintptr_t xa = (uintptr_t)x, qa = (uintptr_t)q;
   if (rows > 0 && ((xa & 15) || (qa & 7))) return set_err(ZIMG_EINVAL, "x must be 16-byte and q 8-byte aligned");
-  HIP_TRY(zimg::launch_quant_rows(x, x_dtype == ZIMG_BF16, ldx, q, ldq, scale, rows, K, (hipStream_t)stream));
+  if (rotate_block != 0 && rotate_block != 128) return set_err(ZIMG_EINVAL, "rotate_block must be 0 or 128");
+  if (rotate_block && K % 128) return set_err(ZIMG_EINVAL, "rotation needs K a multiple of 128");
+  HIP_TRY(zimg::launch_quant_rows(x, x_dtype == ZIMG_BF16, ldx, q, ldq, scale, rows, K, rotate_block != 0, 1.0f,
+                                  (hipStream_t)stream));
   return ZIMG_OK;
 }
 

@@ -124,9 +124,11 @@ hipError_t launch_fold_mod(const float* mod, int64_t mod_stride, const float* no
                            int n_blocks, int n_mod, int D, int B, float* fold, hipStream_t s);
 
 // Rows of width K (K % 8 == 0, K <= 16384) of bf16 or fp32 values, row
-// stride ldx -> int8 codes (row stride ldq) and one scale per row.
+// stride ldx -> int8 codes (row stride ldq) and one scale per row, times
+// post_scale (a power of two).  rotate: each 128 values of a row first go
+// through the unnormalised fast Walsh-Hadamard transform (K % 128 == 0).
 hipError_t launch_quant_rows(const void* x, int x_bf16, int64_t ldx, int8_t* q, int64_t ldq, float* scale, int rows,
-                             int K, hipStream_t s);
+                             int K, int rotate, float post_scale, hipStream_t s);
 
 // Caption features (fp32 or bf16 rows of width Dc) -> bf16 RMSNorm(x; w).
 hipError_t launch_rows_rmsnorm(const void* x, int x_bf16, const float* w, bf16_t* out,

@@ -199,13 +199,17 @@ __global__ __launch_bounds__(256) void rows_rmsnorm_kernel(const void* x, const 
 // Per-row int8 quantization of bf16 or fp32 rows of width K (K % 8 == 0,
 // K <= 8 * 256 * QMAXC): one workgroup per row holds the row in registers
 // (16-byte chunks c = tid + 256 i), reduces max |v|, then writes 8 codes per
-// chunk and the row's scale.  Same arithmetic as the norm kernels' int8
-// output.
+// chunk and the row's scale (times post_scale, a power of two).  Same
+// arithmetic as the norm kernels' int8 output.  ROT: every 128 consecutive
+// values first go through the unnormalised fast Walsh-Hadamard transform in
+// fp32, butterflies (a, b) -> (a + b, a - b) of stride 1, 2, 4 (within a
+// thread's 8 values) then 8, 16, 32, 64 (across the 16 lanes holding the
+// block, lane stride 1, 2, 4, 8); K % 128 == 0.
 constexpr int QMAXC = 8;
-template <bool BF16_IN>
+template <bool BF16_IN, bool ROT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
                                                          int8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
-                                                         int K) {
+                                                         int K, float post_scale) {
   __shared__ float red[8];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int nch = K >> 3;
@@ -214,6 +218,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 #pragma unroll
   for (int i = 0; i < QMAXC; ++i) {
     const int c = tid + 256 * i;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[i][k] = 0.f;
     if (c < nch) {
       if constexpr (BF16_IN) {
         const u32x4 u = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(x) + r * ldx + c * 8);
@@ -228,6 +234,30 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
         v[i][0] = a.x, v[i][1] = a.y, v[i][2] = a.z, v[i][3] = a.w;
         v[i][4] = b.x, v[i][5] = b.y, v[i][6] = b.z, v[i][7] = b.w;
       }
+    }
+    if constexpr (ROT) {
+      // all lanes take part in the shuffles; a 16-lane group is either wholly
+      // inside the row or wholly past it (nch is a multiple of 16)
+#pragma unroll
+      for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (!(k & h)) {
+            const float a = v[i][k], b = v[i][k + h];
+            v[i][k] = a + b;
+            v[i][k + h] = a - b;
+          }
+#pragma unroll
+      for (int lh = 1; lh < 16; lh <<= 1) {
+        const bool upper = (tid & lh) != 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float o = __shfl_xor(v[i][k], lh, 64);
+          v[i][k] = upper ? o - v[i][k] : v[i][k] + o;
+        }
+      }
+    }
+    if (c < nch) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         am = fmaxf(am, fabsf(v[i][k]));
@@ -254,7 +284,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
       *reinterpret_cast<u32x2*>(q + r * ldq + c * 8) = o;
     }
   }
-  if (tid == 0) s[r] = sc;
+  if (tid == 0) s[r] = sc * post_scale;
 }
 
 __global__ void patchify_kernel(const float* lat, bf16_t* out, int B, int C, int Hp, int Wp, int p,
@@ -290,12 +320,15 @@ hipError_t launch_post_norm(const PostNormArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quant_rows(const void* x, int x_bf16, int64_t ldx, int8_t* q, int64_t ldq, float* scale, int rows,
-                             int K, hipStream_t s) {
+                             int K, int rotate, float post_scale, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (x_bf16)
-    hipLaunchKernelGGL(quant_rows_kernel<true>, dim3(rows), dim3(256), 0, s, x, ldx, q, ldq, scale, K);
-  else
-    hipLaunchKernelGGL(quant_rows_kernel<false>, dim3(rows), dim3(256), 0, s, x, ldx, q, ldq, scale, K);
+#define QR(B, R) hipLaunchKernelGGL((quant_rows_kernel<B, R>), dim3(rows), dim3(256), 0, s, x, ldx, q, ldq, scale, K, post_scale)
+  if (x_bf16) {
+    if (rotate) QR(true, true); else QR(true, false);
+  } else {
+    if (rotate) QR(false, true); else QR(false, false);
+  }
+#undef QR
   return hipGetLastError();
 }
 

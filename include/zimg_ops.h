@@ -85,13 +85,21 @@ int zimg_gemm_i8(const void* A, int64_t lda, const float* sa, const void* W, int
  * to weights and activations): for row r with amax = max_k |x[r][k]|,
  * scale[r] = amax / 127 and inv = 127 / amax (each a correctly rounded fp32
  * division), q[r][k] = rint(x[r][k] * inv) (fp32 product, ties to even)
- * clamped to [-127, 127]; a row of zeros gets scale 0 and codes 0.
+ * clamped to [-127, 127]; a row of zeros gets scale 0 and codes 0, a row
+ * holding NaN or an infinity a NaN scale.  rotate_block 128: every 128
+ * consecutive values are first replaced by their unnormalised fast
+ * Walsh-Hadamard transform in fp32 (butterflies (a, b) -> (a + b, a - b) of
+ * stride 1, 2, ..., 64 in that order), the rotation the int8 projections
+ * apply to w2's input and weight rows (after the ConvRot int8 model of
+ * "Z-Image-Turbo, repackaged for H3ddle", What was changed: the activation
+ * is rotated); 0: no rotation.
  * x DEVICE [rows, K] fp32 or bf16 (x_dtype; row stride ldx, 16-byte
  * aligned), q DEVICE int8 (row stride ldq, 8-byte aligned), scale DEVICE
- * fp32 [rows].  K % 8 == 0, K <= 16384, ldx and ldq multiples of 8.
+ * fp32 [rows].  K % 8 == 0 (% 128 with rotation), K <= 16384, ldx and ldq
+ * multiples of 8.
  */
 int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, int64_t ldq, float* scale,
-                       int32_t rows, int32_t K, void* stream);
+                       int32_t rows, int32_t K, int32_t rotate_block, void* stream);
 
 /*
  * Euler update of the FlowMatch sampler: x[i] += dt * (-model_out[i]) for

@@ -72,9 +72,14 @@ def _rows(rows, K, seed):
 
 @pytest.mark.parametrize("rows,K", [(37, 3840), (5, 10240), (4, 136), (3, 16384)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quantize_rows_bit_exact(rows, K, dtype):
+@pytest.mark.parametrize("rotate", [0, 128])
+def test_quantize_rows_bit_exact(rows, K, dtype, rotate):
+    """Codes and scales bit-exact, plain and after the 128-point fast
+    Walsh-Hadamard rotation (the same fp32 butterflies in the same order)."""
     torch = _torch()
     from diffusion_transformer_image_amd import binding
+    if rotate and K % 128:
+        pytest.skip("rotation needs K % 128 == 0")
     x = _rows(rows, K, seed=rows * K)
     if dtype == "bf16":
         x = qz.to_bf16(x)
@@ -83,9 +88,9 @@ def test_quantize_rows_bit_exact(rows, K, dtype):
         xd = torch.from_numpy(x).cuda()
     q = torch.empty((rows, K), dtype=torch.int8, device="cuda")
     s = torch.empty(rows, device="cuda")
-    binding.quantize_rows(xd, q, s)
+    binding.quantize_rows(xd, q, s, rotate_block=rotate)
     torch.cuda.synchronize()
-    wq, ws = qz.quantize_rows(x)
+    wq, ws = qz.quantize_rotated_rows(x) if rotate else qz.quantize_rows(x)
     assert np.array_equal(s.cpu().numpy(), ws)
     assert np.array_equal(q.cpu().numpy(), wq)
 
@@ -113,6 +118,10 @@ def test_quantize_rows_argument_errors():
     with pytest.raises(binding.ZimgError) as ei:
         binding.quantize_rows(torch.zeros((4, 65), device="cuda")[:, 1:], q, s)  # misaligned rows
     assert ei.value.code == binding.ZIMG_EINVAL
+    for rot in (64, 128):  # 64 is no supported block; 64 values are no whole 128-block
+        with pytest.raises(binding.ZimgError) as ei:
+            binding.quantize_rows(torch.zeros((4, 64), device="cuda"), q, s, rotate_block=rot)
+        assert ei.value.code == binding.ZIMG_EINVAL
 
 
 # ---------------------------------------------------------------- GEMM
