@@ -32,19 +32,25 @@ def _torch():
     return torch
 
 
-def _engine(model, max_batch, max_img, max_cap, outlier_log2):
+def _engine(model, max_batch, max_img, max_cap, outlier_log2, **extra):
     from diffusion_transformer_image_amd import binding
     ecfg = helpers.engine_config(model, max_batch=max_batch, max_image_tokens=max_img,
-                                 max_caption_tokens=max_cap)
+                                 max_caption_tokens=max_cap, **extra)
     W = helpers.engine_weights(ecfg, outlier_log2=outlier_log2)
     return binding.DiT(ecfg, W.items_parallel(as_bits=True))
 
 
-def test_euler_loop_reduced_width_vs_oracle():
+@pytest.mark.parametrize("quant", [None, "int8"])
+def test_euler_loop_reduced_width_vs_oracle(quant):
+    """bf16: every step's model output and the final latent at the parity
+    bar.  int8 block projections: against the oracle's int8 loop at the int8
+    bar (tests/test_gpu_int8.py derives it), and the final latent against the
+    float oracle's at the pages' int8 quality figure (cosine >= 0.9996)."""
     torch = _torch()
     from diffusion_transformer_image_amd import euler_loop
+    from tests.test_gpu_int8 import I8_COS_TOL, I8_REL_TOL, INT8_COS_GATE
     lens, shape, log2 = (77, 300), (2, 16, 48, 32), 20
-    dit = _engine(REDUCED, 2, 24 * 16, 300, log2)
+    dit = _engine(REDUCED, 2, 24 * 16, 300, log2, linear_int8=1 if quant else 0)
     lat = synthetic.latent(shape, seed=5)
     caps = synthetic.captions(lens, seed=5)
     x = torch.from_numpy(lat).cuda()
@@ -61,15 +67,22 @@ def test_euler_loop_reduced_width_vs_oracle():
     outs_ref = []
 
     def model_fn(xx, tt):
-        return om.forward(ocfg, Wo, xx, caps, tt, ffn_peak=peaks if not outs_ref else None)
+        return om.forward(ocfg, Wo, xx, caps, tt, ffn_peak=peaks if not outs_ref else None, quant=quant)
 
     ref = osm.run(model_fn, lat, n_steps=8, shift=3.0, on_step=lambda k, xx, o: outs_ref.append(o))
     # heavy-tailed FFN outputs were present (the outlier channels dominate)
     assert max(peaks) > 1e5, f"w2 output peak {max(peaks):.3g}"
+    tol = (I8_REL_TOL, I8_COS_TOL) if quant else (helpers.REL_L2_TOL, helpers.COS_TOL)
     for k in range(8):
-        helpers.assert_parity(outs_gpu[k], outs_ref[k], f"step {k} model output")
-    r, c = helpers.assert_parity(got, ref, "final latent after 8 steps")
-    print(f"w2 output peak {max(peaks):.3g}; final latent rel-L2 {r:.2e} cos {c:.7f}")
+        helpers.assert_parity(outs_gpu[k], outs_ref[k], f"step {k} model output", *tol)
+    r, c = helpers.assert_parity(got, ref, "final latent after 8 steps", *tol)
+    msg = f"w2 output peak {max(peaks):.3g}; final latent rel-L2 {r:.2e} cos {c:.7f}"
+    if quant:
+        ref_f = osm.run(lambda xx, tt: om.forward(ocfg, Wo, xx, caps, tt), lat, n_steps=8, shift=3.0)
+        cf = helpers.cosine(got, ref_f)
+        assert cf >= INT8_COS_GATE, f"final latent cosine {cf:.6f} against the float oracle's loop"
+        msg += f"; vs the float loop cos {cf:.7f}"
+    print(msg)
     dit.close()
 
 
