@@ -206,6 +206,39 @@ __global__ __launch_bounds__(256) void rows_rmsnorm_kernel(const void* x, const 
 // thread's 8 values) then 8, 16, 32, 64 (across the 16 lanes holding the
 // block, lane stride 1, 2, 4, 8); K % 128 == 0.
 constexpr int QMAXC = 8;
+
+// v from lane (lane ^ M) of the same 16-lane row, by DPP moves: quad
+// permutations for 1 and 2 (and 3), a half-row mirror (lane ^ 7) after a
+// quad xor 3 for 4, a row rotation by 8 for 8 (every source lane is inside
+// the row, so bound_ctrl never applies)
+template <int CTRL>
+ZI_DEV float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int M>
+ZI_DEV float lane_xor(float v) {
+  if constexpr (M == 1) return dpp_mov<0xb1>(v);                 // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_mov<0x4e>(v);            // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_mov<0x141>(dpp_mov<0x1b>(v));  // quad [3,2,1,0], half-row mirror
+  else return dpp_mov<0x128>(v);                                 // row_ror:8
+}
+// one cross-lane butterfly stage (lane stride M) on all chunks a thread holds
+// (slots i >= ni hold no chunk of any thread; ni is uniform)
+// The lower lane of a pair keeps a + b, the upper a - b (a: the lower's
+// value); both are the partner's value o plus this lane's value v times
+// sg = +-1, one fma after the DPP move (v * sg is exact, so the fma rounds
+// once, as o + v or o - v does).
+template <int M>
+ZI_DEV void rot_stage(float (&v)[QMAXC][8], int tid, int ni) {
+  const float sg = (tid & M) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < QMAXC; ++i) {
+    if (i >= ni) break;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[i][k] = fmaf(v[i][k], sg, lane_xor<M>(v[i][k]));
+  }
+}
+
 template <bool BF16_IN, bool ROT>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t ldx,
                                                          int8_t* __restrict__ q, int64_t ldq, float* __restrict__ s,
@@ -236,8 +269,6 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
       }
     }
     if constexpr (ROT) {
-      // all lanes take part in the shuffles; a 16-lane group is either wholly
-      // inside the row or wholly past it (nch is a multiple of 16)
 #pragma unroll
       for (int h = 1; h < 8; h <<= 1)
 #pragma unroll
@@ -247,16 +278,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
             v[i][k] = a + b;
             v[i][k + h] = a - b;
           }
-#pragma unroll
-      for (int lh = 1; lh < 16; lh <<= 1) {
-        const bool upper = (tid & lh) != 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float o = __shfl_xor(v[i][k], lh, 64);
-          v[i][k] = upper ? o - v[i][k] : v[i][k] + o;
-        }
-      }
     }
+  }
+  if constexpr (ROT) {
+    // strides 8..64: the partner value sits in lane tid ^ 1, 2, 4, 8 of the
+    // same 16-lane DPP row; every lane takes part (a 16-lane group is wholly
+    // inside the row or wholly past it: nch is a multiple of 16)
+    const int ni = (nch + 255) >> 8;
+    rot_stage<1>(v, tid, ni);
+    rot_stage<2>(v, tid, ni);
+    rot_stage<4>(v, tid, ni);
+    rot_stage<8>(v, tid, ni);
+  }
+#pragma unroll
+  for (int i = 0; i < QMAXC; ++i) {
+    const int c = tid + 256 * i;
     if (c < nch) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
