@@ -14,8 +14,8 @@
 // Workgroup tile BM x BN, K-step 64, 512 threads = 8 waves (2 waves per
 // SIMD, so one wave's MFMAs cover the other's memory waits).  Operands go
 // global -> LDS directly (global_load_lds_dwordx4, no register staging) into
-// a two-stage ring: the next K-step's loads are issued at the start of the
-// current one, and one barrier per K-step publishes them.  LDS rows are
+// a two-stage ring: the next K-step's loads are issued early in the current
+// one, and one barrier per K-step publishes them.  LDS rows are
 // 128 B (64 bf16); the 16-byte chunk c of row r
 // is stored at position c ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 B
 // per cycle, and with two rows per 256-byte bank line this makes the 16
@@ -36,7 +36,17 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int NT = 512;
-constexpr int GROUP_M = 8;
+
+// Tile order: groups of gm row-tiles, column-major inside a group, so the
+// tiles that run together on one XCD share row and column panels in its L2.
+// gm is chosen per projection (group_rows below).
+ZI_DEV void grouped_tile(int lid, int tiles_m, int tiles_n, int gm, int& tm, int& tn) {
+  const int per_group = gm * tiles_n;
+  const int first_m = (lid / per_group) * gm;
+  const int gsize = min(tiles_m - first_m, gm);
+  tm = first_m + (lid % per_group) % gsize;
+  tn = (lid % per_group) / gsize;
+}
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -323,7 +333,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int ROLE, bool I8>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ A, int64_t lda,
                                                      const bf16_t* __restrict__ W, int64_t ldw,
                                                      int M, int N, int K, EpiArgs ep, int tiles_m,
-                                                     int tiles_n, int full_tiles, int nsplit, float* ws) {
+                                                     int tiles_n, int full_tiles, int nsplit, float* ws, int gm) {
   static_assert(WM * WN == NT / 64, "8 waves");
   constexpr int NW = NT / 64;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -354,11 +364,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   const int tail_idx = is_split ? (uid - full_tiles) / nsplit : 0;
   const int chunk = is_split ? (uid - full_tiles) - tail_idx * nsplit : 0;
   const int lid = is_split ? full_tiles + tail_idx : uid;  // tile id in grouped order
-  const int per_group = GROUP_M * tiles_n;
-  const int first_m = (lid / per_group) * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int tm = first_m + (lid % per_group) % gsize;
-  const int tn = (lid % per_group) / gsize;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, tiles_n, gm, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -495,7 +502,8 @@ constexpr int RED_PER_THREAD = 4;
 
 template <int BM, int BN, int WM, int WN, int EPI, bool I8>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs ep, int tiles_m, int tiles_n,
-                                                          int full_tiles, int nsplit, const float* __restrict__ ws) {
+                                                          int full_tiles, int nsplit, const float* __restrict__ ws,
+                                                          int gm) {
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
   constexpr int TILE_F = BM * BN;
   constexpr int SLOTS = (EPI == EPI_SWIGLU) ? TILE_F / 2 : TILE_F;  // outputs per tile
@@ -503,11 +511,9 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
   constexpr int WG_PER_TILE = SLOTS / PER_WG;
   const int tail_idx = blockIdx.x / WG_PER_TILE;
   const int lid = full_tiles + tail_idx;
-  const int per_group = GROUP_M * tiles_n;
-  const int first_m = (lid / per_group) * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int m0 = (first_m + (lid % per_group) % gsize) * BM;
-  const int n0 = ((lid % per_group) / gsize) * BN;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, tiles_n, gm, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F;
   int qs[RED_PER_THREAD];
 #pragma unroll
@@ -579,18 +585,17 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs 
 // l and l + 32 hold 4 + 4 consecutive rows of one column).
 template <int BM, int BN, int WM, int WN, bool I8>
 __global__ __launch_bounds__(256) void gemm_qkv_reduce_kernel(int M, EpiArgs ep, int tiles_m, int tiles_n,
-                                                              int full_tiles, int nsplit, const float* __restrict__ ws) {
+                                                              int full_tiles, int nsplit, const float* __restrict__ ws,
+                                                              int gm) {
   static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "QKV epilogue tiling");
   constexpr int TM = 4, TN = 2, TILE_F = BM * BN;
   __shared__ __attribute__((aligned(16))) bf16_t st[32 * 256];
   const int tail_idx = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int wm = slice >> 2, i = slice & 3;  // rows wm*128 + i*32 .. +31 of the tile
   const int lid = full_tiles + tail_idx;
-  const int per_group = GROUP_M * tiles_n;
-  const int first_m = (lid / per_group) * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int m0 = (first_m + (lid % per_group) % gsize) * BM;
-  const int n0 = ((lid % per_group) / gsize) * BN;
+  int tm, tn;
+  grouped_tile(lid, tiles_m, tiles_n, gm, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, wn = tid >> 6, lane = tid & 63, lrow = lane & 31, lhalf = lane >> 5;
   const int src_tid = (wm * WN + wn) * 64 + lane;
   const float* part = ws + (int64_t)tail_idx * nsplit * TILE_F + src_tid;
@@ -688,6 +693,21 @@ int choose_split(int T, int KT, int tile_bytes, const GemmSplit& sp) {
   return best;
 }
 
+// Row-tiles per group of the tile order, per projection.  32 tiles run at
+// once on each XCD (256 CUs, 8 XCDs, one workgroup per CU), so a group of gm
+// rows spans about 32 / gm columns; which split shares its L2 best depends on
+// the number of column tiles (80 for w1|w3, 45 for qkv, 15 for out and w2),
+// and was chosen by measuring the forward with each value.
+int group_rows(int role, int tiles_n) {
+  switch (role) {
+    case ROLE_QKV: return 3;
+    case ROLE_W13: return 2;
+    case ROLE_OUT:
+    case ROLE_W2: return 6;
+    default: return tiles_n >= 32 ? 3 : 6;
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE, bool I8>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   static_assert(2 * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
@@ -698,24 +718,25 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const int K = g.K / U;
   GemmSplit sp = g.split;
   sp.n_cu *= (160 * 1024) / LDS_BYTES;  // workgroups resident at once
+  const int gm = group_rows(ROLE, tiles_n);
   const int nsplit = choose_split(T, K / BK, BM * BN * 4, sp);
   const int full = nsplit > 1 ? T - T % sp.n_cu : T;
   const int units = full + (T - full) * nsplit;
   hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI, ROLE, I8>), dim3(units), dim3(NT), 0, s,
                      (const bf16_t*)g.A, g.lda / U, (const bf16_t*)g.W, g.ldw / U, g.M, g.N, K, g.ep, tiles_m,
-                     tiles_n, full, nsplit, g.split.ws);
+                     tiles_n, full, nsplit, g.split.ws, gm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   if constexpr (EPI == EPI_QKV_ROPE) {
     hipLaunchKernelGGL((gemm_qkv_reduce_kernel<BM, BN, WM, WN, I8>), dim3((T - full) * 8), dim3(256), 0, s, g.M,
-                       g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws);
+                       g.ep, tiles_m, tiles_n, full, nsplit, g.split.ws, gm);
     return hipGetLastError();
   }
   constexpr int SLOTS = (EPI == EPI_SWIGLU) ? BM * BN / 2 : BM * BN;
   static_assert(SLOTS % (256 * RED_PER_THREAD) == 0, "reduce grid");
   hipLaunchKernelGGL((gemm_reduce_kernel<BM, BN, WM, WN, EPI, I8>),
                      dim3((T - full) * (SLOTS / (256 * RED_PER_THREAD))), dim3(256), 0, s, g.M, g.N, g.ep, tiles_m,
-                     tiles_n, full, nsplit, g.split.ws);
+                     tiles_n, full, nsplit, g.split.ws, gm);
   return hipGetLastError();
 }
 
