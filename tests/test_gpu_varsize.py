@@ -150,3 +150,30 @@ def test_varsize_argument_errors():
         assert ei.value.code == binding.ZIMG_EINVAL and msg in str(ei.value), str(ei.value)
     with pytest.raises(ValueError):
         dit.forward_varsize(lat_d, caps_d, LENS, TIMES, outs[:2])
+
+
+def test_varsize_batch_int8_projections():
+    """The mixed batch with int8 block projections: each sample's output
+    against the oracle's int8 variant on that sample alone (int8 bar) and
+    against the float oracle (the pages' int8 cosine)."""
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    from tests.test_gpu_int8 import I8_COS_TOL, I8_REL_TOL, INT8_COS_GATE
+    n_max = max((h // 2) * (w // 2) for h, w in SIZES)
+    ecfg = helpers.engine_config(SMALL, max_batch=3, max_image_tokens=n_max, max_caption_tokens=max(LENS),
+                                 linear_int8=1)
+    dit = binding.DiT(ecfg, helpers.engine_weights(ecfg, seed=7).items_parallel(as_bits=True))
+    lats, caps, lat_d, caps_d = _inputs()
+    outs = [torch.empty_like(x) for x in lat_d]
+    dit.forward_varsize(lat_d, caps_d, LENS, TIMES, outs)
+    torch.cuda.synchronize()
+    dit.close()
+    ocfg = helpers.oracle_config(SMALL)
+    Wo = helpers.oracle_weights(SMALL, seed=7).materialize(workers=4)
+    for b in range(3):
+        t32 = float(np.float32(TIMES[b]))
+        got = outs[b].cpu().numpy()
+        ref_q = om.forward_sample(ocfg, Wo, lats[b], caps[b], t32, quant="int8")
+        helpers.assert_parity(got, ref_q, f"sample {b} vs the int8 oracle", I8_REL_TOL, I8_COS_TOL)
+        cf = helpers.cosine(got, om.forward_sample(ocfg, Wo, lats[b], caps[b], t32))
+        assert cf >= INT8_COS_GATE, f"sample {b}: cosine {cf:.6f} against the float oracle"
