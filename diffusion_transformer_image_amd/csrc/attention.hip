@@ -40,6 +40,21 @@ constexpr int AHEAD = 3;               // LDS operand reads issued ahead of thei
 
 ZI_DEV int swap_bits23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Lanes l and l ^ 32 hold the two key halves of one query.  v_permlane32_swap
+// exchanges the 32-lane halves of two registers, so with both operands v the
+// results hold v of lanes 0-31 and v of lanes 32-63 in every lane: the pair
+// combines in registers, without an LDS round trip, and in the same order on
+// both lanes.
+ZI_DEV float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float lo = __uint_as_float(r[0]), hi = __uint_as_float(r[1]);
+  return lo > hi ? lo : hi;
+}
+ZI_DEV float pair_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // K tiles [64 keys][128] and V^T tiles [128][64 keys], two of each
   __shared__ __attribute__((aligned(16))) bf16_t K0[KTILE * HD];
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[tt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    mx = pair_max(mx) * sl2;
     const float mnew = mx > m + RESCALE_SLACK ? mx : m;
     if (__any(mnew != m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
         st[tt][e] = p;
         rs += p;
       }
-    l += rs + __shfl_xor(rs, 32, 64);
+    l += rs;  // this lane's keys only; the pair is summed once, at the end
   };
   // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
   auto pv = [&](const bf16_t* vb, const f32x16* st) {
@@ -279,6 +294,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     half(K0, V1, sn, sc, nvalid(j + 1));  // j + 1 == tn: the padding tile, fully masked
   }
 
+  l = pair_sum(l);
   if (qi < it.nq && unit >= 0) {
     // partial state of this chunk: O unnormalised (relative to 2^m), m, l
     float* po = a.part + (int64_t)unit * (128 * HD) + qi * HD;
