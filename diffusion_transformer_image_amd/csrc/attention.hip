@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, lp[4] = {0.f, 0.f, 0.f, 0.f};
   const float sl2 = a.scale_log2;
 
   // Online softmax in the log2 domain (raw v_exp_f32: weights below 2^-126
@@ -196,7 +196,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     const float mnew = mx > m + RESCALE_SLACK ? mx : m;
     if (__any(mnew != m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      l *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lp[i] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -204,17 +205,17 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       m = mnew;
     }
   };
+  // the row sum of this lane's keys in four running parts (short dependency
+  // chains); the parts and the lane pair are summed once, at the end
   auto expsum = [&](f32x16* st) {
-    float rs = 0.f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], sl2, -m));
         st[tt][e] = p;
-        rs += p;
+        lp[e & 3] += p;
       }
-    l += rs;  // this lane's keys only; the pair is summed once, at the end
   };
   // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
   auto pv = [&](const bf16_t* vb, const f32x16* st) {
@@ -266,6 +267,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     expsum(scur);
     pv(vc, scur);
     pin_order();
+    // keeps the row-sum additions inside this half's interleave (otherwise
+    // they are sunk past the next barrier, into the next half's serial part)
+    asm volatile("" : "+v"(lp[0]), "+v"(lp[1]), "+v"(lp[2]), "+v"(lp[3]));
   };
 
   // The tile count is padded to an even number (>= 2) with an empty tile: its
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     half(K0, V1, sn, sc, nvalid(j + 1));  // j + 1 == tn: the padding tile, fully masked
   }
 
-  l = pair_sum(l);
+  const float l = pair_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
   if (qi < it.nq && unit >= 0) {
     // partial state of this chunk: O unnormalised (relative to 2^m), m, l
     float* po = a.part + (int64_t)unit * (128 * HD) + qi * HD;
