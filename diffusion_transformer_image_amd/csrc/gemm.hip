@@ -413,57 +413,77 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < TN; ++j) bfr[set][j] = *reinterpret_cast<const bf16x8*>(bs + boff + j * 32 * BK + ch);
   };
-  // One K-step: the operand reads of the first k16 step, then the next
-  // stage's loads (issued after those reads; issued before them, the kernel
-  // measured 2-6 % slower), then four k16 steps in
-  // which the operand reads of step k+1 are interleaved one-for-one with the
-  // MFMAs of step k (the scheduling barriers pin that order), so LDS latency
-  // hides behind matrix-core work.
-  auto step = [&](const bf16_t* as, const bf16_t* bs, bool do_issue, int kt_next, bf16_t* nas, bf16_t* nbs) {
-    frags(as, bs, 0, 0);
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (I8)
+          acc[i][j] = mfma32_i8(af[set][i], bfr[set][j], acc[i][j]);
+        else
+          acc[i][j] = mfma32(af[set][i], bfr[set][j], acc[i][j]);
+      }
+  };
+  constexpr int PAIRS = (TM + TN) < (TM * TN) ? (TM + TN) : (TM * TN);
+  auto pin_pairs = [&]() {  // MFMAs of one k16 step, one-for-one with the next step's operand reads
+#pragma unroll
+    for (int g = 0; g < PAIRS; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    if (TM + TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN - PAIRS, 0);
+    if (TM * TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - PAIRS, 0);
+  };
+  // One K-step, entered with the operands of its first k16 step in set 0:
+  // the MFMAs of the previous K-step's last k16 step (held back, operands in
+  // set 1; they cover the latency of the set-0 reads issued just before),
+  // the next stage's loads, then three k16 steps whose MFMAs are interleaved
+  // one-for-one with the operand reads of the step after (the scheduling
+  // barriers pin that order).  The fourth k16 step's MFMAs are held back
+  // past the barrier that ends the K-step, behind the next stage's first
+  // operand reads.
+  auto step = [&](const bf16_t* as, const bf16_t* bs, bool prev_tail, bool do_issue, int kt_next, bf16_t* nas,
+                  bf16_t* nbs) {
+    if (prev_tail) mfmas(1);
     if (do_issue) issue(kt_next, nas, nbs);
-    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of step 0
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of the first k16 step (before the call)
+    if (prev_tail) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // held-back MFMAs
     __builtin_amdgcn_sched_group_barrier(0x020, NA + NB, 0);  // VMEM (the loads above)
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) frags(as, bs, kk + 1, (kk + 1) & 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          if constexpr (I8)
-            acc[i][j] = mfma32_i8(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
-          else
-            acc[i][j] = mfma32(af[kk & 1][i], bfr[kk & 1][j], acc[i][j]);
-        }
-      if (kk + 1 < BK / 16) {
-        constexpr int PAIRS = (TM + TN) < (TM * TN) ? (TM + TN) : (TM * TN);
-#pragma unroll
-        for (int g = 0; g < PAIRS; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
-        if (TM + TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, TM + TN - PAIRS, 0);
-        if (TM * TN > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - PAIRS, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
-      }
+    for (int kk = 0; kk + 1 < BK / 16; ++kk) {
+      frags(as, bs, kk + 1, (kk + 1) & 1);
+      mfmas(kk & 1);
+      pin_pairs();
     }
   };
 
   const int KTALL = K / BK;
   const int kt0 = is_split ? (int)((int64_t)chunk * KTALL / nsplit) : 0;
   const int KT = is_split ? (int)((int64_t)(chunk + 1) * KTALL / nsplit) : KTALL;
+  // K-steps alternate between the two buffers; every step except a lone
+  // last one issues loads, so the loop body has no branch that would keep
+  // them from interleaving with the MFMAs (where no stage is left to load,
+  // the step reloads its own stage into the free buffer: waited for by the
+  // next barrier, never read).
   issue(kt0, As0, Bs0);
   dma_barrier();
-  int kt = kt0;
+  frags(As0, Bs0, 0, 0);
+  step(As0, Bs0, false, true, kt0 + 1 < KT ? kt0 + 1 : kt0, As1, Bs1);
+  dma_barrier();
+  int kt = kt0 + 1;
   for (; kt + 2 <= KT; kt += 2) {
-    step(As0, Bs0, true, kt + 1, As1, Bs1);
+    frags(As1, Bs1, 0, 0);
+    step(As1, Bs1, true, true, kt + 1, As0, Bs0);
     dma_barrier();
-    step(As1, Bs1, kt + 2 < KT, kt + 2, As0, Bs0);
+    frags(As0, Bs0, 0, 0);
+    step(As0, Bs0, true, true, kt + 2 < KT ? kt + 2 : kt + 1, As1, Bs1);
     dma_barrier();
   }
-  if (kt < KT) step(As0, Bs0, false, 0, As1, Bs1);
+  if (kt < KT) {
+    frags(As1, Bs1, 0, 0);
+    step(As1, Bs1, true, false, 0, As0, Bs0);
+  }
+  mfmas(1);  // the last K-step's fourth k16 step
 
   if (is_split) {
     // A split unit stores its partial (accumulator order, lanes contiguous;
