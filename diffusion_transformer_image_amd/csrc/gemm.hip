@@ -374,25 +374,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   // A wave's load i fills 1 KB of LDS = 64 chunks of 16 B, chunk p = (i*NW + wid)*64 + lane,
   // i.e. row p/8, stored position p%8; it fetches the logical chunk stored there
   // (rows past M or N are clamped: their results are never stored).
-  const bf16_t* a_src[NA];
+  // Sources are a per-tile base (uniform: scalar registers) plus a per-lane
+  // 32-bit byte offset that stays fixed for the whole K loop, so the loads
+  // take the scalar-base form and a K-step only advances the two bases.
+  const char* a_base = reinterpret_cast<const char*>(A + (int64_t)m0 * lda);
+  const char* b_base = reinterpret_cast<const char*>(W + (int64_t)n0 * ldw);
+  uint32_t a_off[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-    a_src[i] = A + (int64_t)min(m0 + row, M - 1) * lda + lc * 8;
+    a_off[i] = (uint32_t)((min(m0 + row, M - 1) - m0) * lda * 2 + lc * 16);
   }
-  const bf16_t* b_src[NB];
+  uint32_t b_off[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
-    b_src[i] = W + (int64_t)min(n0 + row, N - 1) * ldw + lc * 8;
+    b_off[i] = (uint32_t)((min(n0 + row, N - 1) - n0) * ldw * 2 + lc * 16);
   }
   auto issue = [&](int kt, bf16_t* as, bf16_t* bs) {
+    const char* ak = a_base + (int64_t)kt * (BK * 2);
+    const char* bk = b_base + (int64_t)kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kt * BK), LDS_PTR(as + (i * NW + wid) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(ak + a_off[i]), LDS_PTR(as + (i * NW + wid) * 512), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kt * BK), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(bk + b_off[i]), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
   };
 
   using AccT = typename AccOf<I8>::T;
@@ -776,6 +783,8 @@ const char* gemm_check(const GemmArgs& g) {
   if (g.epi == EPI_SWIGLU && g.N % 256) return "gemm: SwiGLU needs N a multiple of 256";
   if (g.lda < g.K || g.ldw < g.K) return "gemm: leading dimension smaller than K";
   if ((g.lda % 8) || (g.ldw % 8)) return "gemm: lda and ldw must be multiples of 8";
+  // a tile's 256 rows must span less than 2^32 bytes (32-bit load offsets)
+  if (g.lda > (1 << 22) || g.ldw > (1 << 22)) return "gemm: lda and ldw must be at most 4194304";
   if ((g.epi == EPI_BF16 || g.epi == EPI_SWIGLU) && ((g.ep.ldc % 8) || ((uintptr_t)g.ep.C & 15)))
     return "gemm: bf16 output needs ldc a multiple of 8 and a 16-byte aligned C";
   if (!g.A || !g.W || !g.ep.C) return "gemm: null pointer";

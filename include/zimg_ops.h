@@ -57,7 +57,8 @@ int zimg_dit_run_blocks(zimg_dit* h, float* x_io, int32_t B, int32_t Hl, int32_t
  * C = epilogue(A W^T): A DEVICE bf16 [M, K] (row stride lda), W DEVICE bf16
  * [N, K] (row stride ldw; a linear layer's weight), C DEVICE with row
  * stride ldc.  Constraints: K % 64 == 0, N % 64 == 0 (N % 256 for SwiGLU),
- * lda, ldw multiples of 8; for bf16 outputs (plain and SwiGLU) ldc a
+ * lda, ldw multiples of 8 and at most 4194304 (2^22); for bf16 outputs
+ * (plain and SwiGLU) ldc a
  * multiple of 8 and C 16-byte aligned.  fp32 accumulation on bf16 MFMA; no
  * scratch.
  */

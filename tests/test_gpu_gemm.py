@@ -122,3 +122,9 @@ def test_gemm_rejects_bad_shapes():
     with pytest.raises(binding.ZimgError) as ei:
         binding.gemm_bf16(A, W, Cw[:, :64])
     assert ei.value.code == binding.ZIMG_EINVAL and "ldc" in str(ei.value)
+    # a row stride past 2^22 elements is refused before any launch (the
+    # pointers are never dereferenced)
+    with pytest.raises(binding.ZimgError) as ei:
+        binding._check(binding.lib().zimg_gemm_bf16(binding._ptr(A), (1 << 22) + 8, binding._ptr(W), 64,
+                                                     binding._ptr(C), 64, 16, 64, 64, binding.EPI_BF16, None, None))
+    assert ei.value.code == binding.ZIMG_EINVAL and "at most 4194304" in str(ei.value)
