@@ -191,6 +191,33 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _want(t, name, dtypes, ndim=None, contiguous=False):
+    """Refuse, before any native call, a tensor the entry point cannot read:
+    not a CUDA tensor, another dtype or rank, or rows that are not unit-stride
+    (or, with ``contiguous``, not one dense block)."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name}: a torch CUDA tensor is required")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} is not one of {tuple(str(d) for d in dtypes)}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: a {ndim}-d tensor is required, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: a contiguous tensor is required")
+    if t.dim() >= 1 and t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name}: rows must be unit-stride")
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _f32_bf16():
+    import torch
+    return (torch.float32, torch.bfloat16)
+
+
 class DiT:
     """Handle of one engine instance (device weights + workspace)."""
 
@@ -230,10 +257,15 @@ class DiT:
     def forward(self, latent, caption_feats, caption_lens, t, out, stream=None):
         """latent, caption_feats, out: torch CUDA tensors (fp32 latent/out,
         fp32 or bf16 packed captions); caption_lens, t: host sequences."""
+        import torch
+        _want(latent, "latent", _f32(), 4, contiguous=True)
+        _want(out, "out", _f32(), 4, contiguous=True)
+        _want(caption_feats, "caption_feats", _f32_bf16(), 2, contiguous=True)
+        if out.shape != latent.shape:
+            raise ValueError("out must have the latent's shape")
         B, C, Hl, Wl = latent.shape
         lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
         tt = np.ascontiguousarray(t, dtype=np.float32)
-        import torch
         cap_dt = ZIMG_BF16 if caption_feats.dtype == torch.bfloat16 else ZIMG_F32
         _check(lib().zimg_dit_forward(self._h, _ptr(latent), B, Hl, Wl, _ptr(caption_feats), cap_dt,
                                       lens.ctypes.data_as(_I32P), tt.ctypes.data_as(_F32P), _ptr(out),
@@ -250,9 +282,11 @@ class DiT:
         hl = np.ascontiguousarray([x.shape[-2] for x in latents], dtype=np.int32)
         wl = np.ascontiguousarray([x.shape[-1] for x in latents], dtype=np.int32)
         for x, o in zip(latents, outs):
-            if x.dtype != torch.float32 or o.dtype != torch.float32 or not x.is_contiguous() or not o.is_contiguous() \
-                    or tuple(o.shape[-3:]) != tuple(x.shape[-3:]):
+            _want(x, "latents", _f32(), contiguous=True)
+            _want(o, "outs", _f32(), contiguous=True)
+            if tuple(o.shape[-3:]) != tuple(x.shape[-3:]):
                 raise ValueError("latents and outs: contiguous fp32 tensors of matching shapes")
+        _want(caption_feats, "caption_feats", _f32_bf16(), 2, contiguous=True)
         lp = (ctypes.c_void_p * B)(*[x.data_ptr() for x in latents])
         op = (ctypes.c_void_p * B)(*[o.data_ptr() for o in outs])
         lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
@@ -264,6 +298,7 @@ class DiT:
         return outs
 
     def run_blocks(self, x, B, Hl, Wl, caption_lens, t, first, n, stream=None):
+        _want(x, "x", _f32(), contiguous=True)
         lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
         tt = np.ascontiguousarray(t, dtype=np.float32)
         _check(lib().zimg_dit_run_blocks(self._h, _ptr(x), B, Hl, Wl, lens.ctypes.data_as(_I32P),
@@ -336,8 +371,27 @@ def rope_tables(cfg, ids):
     return cs, sn
 
 
+def _gemm_out_checks(A, W, C, epilogue, bias):
+    import torch
+    if A.shape[1] != W.shape[1]:
+        raise ValueError(f"A and W disagree on K: {tuple(A.shape)} vs {tuple(W.shape)}")
+    out_dt = (torch.float32,) if epilogue == EPI_F32_BIAS else (torch.bfloat16,)
+    _want(C, "C", out_dt, 2)
+    n_out = W.shape[0] // 2 if epilogue == EPI_SWIGLU else W.shape[0]
+    if C.shape[0] != A.shape[0] or C.shape[1] != n_out:
+        raise ValueError(f"C must be [{A.shape[0]}, {n_out}], got {tuple(C.shape)}")
+    if bias is not None:
+        _want(bias, "bias", _f32(), 1, contiguous=True)
+        if bias.numel() != W.shape[0]:
+            raise ValueError("bias: one value per output column")
+
+
 def gemm_bf16(A, W, C, epilogue=EPI_BF16, bias=None, stream=None):
     """C = epilogue(A W^T) on torch CUDA tensors (A, W bf16; C bf16 or fp32)."""
+    import torch
+    _want(A, "A", (torch.bfloat16,), 2)
+    _want(W, "W", (torch.bfloat16,), 2)
+    _gemm_out_checks(A, W, C, epilogue, bias)
     M, K = A.shape
     N = W.shape[0]
     _check(lib().zimg_gemm_bf16(_ptr(A), A.stride(0), _ptr(W), W.stride(0), _ptr(C), C.stride(0), M, N, K,
@@ -348,6 +402,14 @@ def gemm_bf16(A, W, C, epilogue=EPI_BF16, bias=None, stream=None):
 def gemm_i8(A, sa, W, sw, C, epilogue=EPI_BF16, bias=None, stream=None):
     """C = epilogue((A W^T) * sa[:, None] * sw[None, :]) on torch CUDA tensors
     (A, W int8 codes; sa, sw fp32 row scales; C bf16 or fp32)."""
+    import torch
+    _want(A, "A", (torch.int8,), 2)
+    _want(W, "W", (torch.int8,), 2)
+    _want(sa, "sa", _f32(), 1, contiguous=True)
+    _want(sw, "sw", _f32(), 1, contiguous=True)
+    if sa.numel() != A.shape[0] or sw.numel() != W.shape[0]:
+        raise ValueError("sa and sw: one scale per row of A and of W")
+    _gemm_out_checks(A, W, C, epilogue, bias)
     M, K = A.shape
     N = W.shape[0]
     _check(lib().zimg_gemm_i8(_ptr(A), A.stride(0), _ptr(sa), _ptr(W), W.stride(0), _ptr(sw), _ptr(C), C.stride(0),
@@ -359,9 +421,14 @@ def quantize_rows(x, q, scale, rotate_block=0, stream=None):
     """Per-row int8 codes q and scales of x (torch CUDA fp32 or bf16 rows),
     after a 128-point Walsh-Hadamard rotation when rotate_block is 128."""
     import torch
-    rows, K = x.shape
-    if x.dtype not in (torch.float32, torch.bfloat16):
+    if isinstance(x, torch.Tensor) and x.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"quantize_rows takes fp32 or bf16 rows, got {x.dtype}")
+    _want(x, "x", _f32_bf16(), 2)
+    _want(q, "q", (torch.int8,), 2)
+    _want(scale, "scale", _f32(), 1, contiguous=True)
+    rows, K = x.shape
+    if tuple(q.shape) != (rows, K) or scale.numel() != rows:
+        raise ValueError("q must have x's shape and scale one value per row")
     dt = ZIMG_BF16 if x.dtype == torch.bfloat16 else ZIMG_F32
     _check(lib().zimg_quantize_rows(_ptr(x), dt, x.stride(0), _ptr(q), q.stride(0), _ptr(scale), rows, K,
                                     rotate_block, _stream(stream)))
@@ -370,11 +437,20 @@ def quantize_rows(x, q, scale, rotate_block=0, stream=None):
 
 def cfg_euler_step(x, out_cond, out_uncond, guidance, dt, stream=None):
     """x += dt * -(out_cond + guidance * (out_cond - out_uncond)) (torch CUDA fp32)."""
+    for name, v in (("x", x), ("out_cond", out_cond), ("out_uncond", out_uncond)):
+        _want(v, name, _f32(), contiguous=True)
+        if v.numel() != x.numel():
+            raise ValueError(f"{name}: {x.numel()} elements required")
     _check(lib().zimg_cfg_euler_step(_ptr(x), _ptr(out_cond), _ptr(out_uncond), float(guidance), float(dt),
                                      x.numel(), _stream(stream)))
     return x
 
 
 def euler_step(x, model_out, dt, stream=None):
+    """x += dt * -model_out (torch CUDA fp32)."""
+    for name, v in (("x", x), ("model_out", model_out)):
+        _want(v, name, _f32(), contiguous=True)
+        if v.numel() != x.numel():
+            raise ValueError(f"{name}: {x.numel()} elements required")
     _check(lib().zimg_euler_step(_ptr(x), _ptr(model_out), float(dt), x.numel(), _stream(stream)))
     return x

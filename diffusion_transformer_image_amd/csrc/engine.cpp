@@ -23,6 +23,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -149,16 +150,19 @@ std::vector<ManifestEntry> build_manifest(const zimg_dit_config& c) {
   return m;
 }
 
-// manifests are cached per config so that entry names stay valid
-std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>>& manifest_cache() {
-  static std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>> m;
-  return m;
-}
+// manifests are cached per config so that entry names stay valid for the
+// life of the process; the cache may be reached from several threads (a
+// manifest query while another thread creates an engine), hence the lock.
+// Entries are never removed, so a returned reference stays valid unlocked.
+// (the key is the config's bytes: 24 four-byte fields, no padding)
+static_assert(sizeof(zimg_dit_config) == 24 * 4, "zimg_dit_config must have no padding");
 const std::vector<ManifestEntry>& cached_manifest(const zimg_dit_config& c) {
-  std::string key((const char*)&c, sizeof c);
-  auto& mc = manifest_cache();
-  auto it = mc.find(key);
-  if (it == mc.end()) it = mc.emplace(key, std::make_unique<std::vector<ManifestEntry>>(build_manifest(c))).first;
+  static std::mutex mu;
+  static std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>> cache;
+  const std::string key((const char*)&c, sizeof c);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it == cache.end()) it = cache.emplace(key, std::make_unique<std::vector<ManifestEntry>>(build_manifest(c))).first;
   return *it->second;
 }
 

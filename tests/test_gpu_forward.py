@@ -184,18 +184,27 @@ def test_forward_argument_errors():
     lat_d = torch.zeros((1, 16, 24, 20), device="cuda")
     caps_d = torch.zeros((50, 2560), device="cuda")
     out = torch.empty_like(lat_d)
+    def run(lat, lens, t):
+        return dit.forward(lat, caps_d, lens, t, torch.empty_like(lat))
+
     bad = [
-        (lambda: dit.forward(torch.zeros((1, 16, 23, 20), device="cuda"), caps_d, (50,), (0.5,), out), "multiples"),
-        (lambda: dit.forward(lat_d, caps_d, (0,), (0.5,), out), "length 0"),
-        (lambda: dit.forward(lat_d, caps_d, (78,), (0.5,), out), "outside 1..77"),
-        (lambda: dit.forward(lat_d, caps_d, (50,), (math.nan,), out), "not finite"),
-        (lambda: dit.forward(torch.zeros((1, 16, 24, 22), device="cuda"), caps_d, (50,), (0.5,), out), "exceed"),
-        (lambda: dit.forward(torch.zeros((2, 16, 24, 20), device="cuda"), caps_d, (50, 50), (0.5, 0.5), out), "batch"),
+        (lambda: run(torch.zeros((1, 16, 23, 20), device="cuda"), (50,), (0.5,)), "multiples"),
+        (lambda: run(lat_d, (0,), (0.5,)), "length 0"),
+        (lambda: run(lat_d, (78,), (0.5,)), "outside 1..77"),
+        (lambda: run(lat_d, (50,), (math.nan,)), "not finite"),
+        (lambda: run(torch.zeros((1, 16, 24, 22), device="cuda"), (50,), (0.5,)), "exceed"),
+        (lambda: run(torch.zeros((2, 16, 24, 20), device="cuda"), (50, 50), (0.5, 0.5)), "batch"),
     ]
     for fn, msg in bad:
         with pytest.raises(binding.ZimgError) as ei:
             fn()
         assert ei.value.code == binding.ZIMG_EINVAL and msg in str(ei.value), str(ei.value)
+    # refused by the binding before any native call: an output of another
+    # shape (the library sees only a pointer), a half-precision latent
+    with pytest.raises(ValueError, match="shape"):
+        dit.forward(lat_d, caps_d, (50,), (0.5,), torch.empty((1, 16, 24, 18), device="cuda"))
+    with pytest.raises(ValueError, match="dtype"):
+        dit.forward(lat_d.half(), caps_d, (50,), (0.5,), out)
 
 
 def test_weight_table_errors():

@@ -122,6 +122,13 @@ def test_gemm_rejects_bad_shapes():
     with pytest.raises(binding.ZimgError) as ei:
         binding.gemm_bf16(A, W, Cw[:, :64])
     assert ei.value.code == binding.ZIMG_EINVAL and "ldc" in str(ei.value)
+    # the binding's own checks: output dtype of the epilogue, K agreement, output shape
+    with pytest.raises(ValueError, match="dtype"):
+        binding.gemm_bf16(A, W, torch.zeros((16, 64), device="cuda"), binding.EPI_BF16)
+    with pytest.raises(ValueError, match="disagree on K"):
+        binding.gemm_bf16(A, torch.zeros((64, 128), dtype=torch.bfloat16, device="cuda"), C)
+    with pytest.raises(ValueError, match="must be"):
+        binding.gemm_bf16(A, W, C, binding.EPI_SWIGLU)
     # a row stride past 2^22 elements is refused before any launch (the
     # pointers are never dereferenced)
     with pytest.raises(binding.ZimgError) as ei:

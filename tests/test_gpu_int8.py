@@ -186,13 +186,14 @@ def test_gemm_i8_argument_errors():
     torch = _torch()
     from diffusion_transformer_image_amd import binding
     a = torch.zeros((64, 256), dtype=torch.int8, device="cuda")
-    s = torch.ones(512, device="cuda")
+    sa = torch.ones(64, device="cuda")
+    sw = torch.ones(512, device="cuda")
     C = torch.empty((64, 512), device="cuda")
     w = torch.zeros((512, 256), dtype=torch.int8, device="cuda")
     bad = [
-        (lambda: binding.gemm_i8(a[:, :192], s, w[:, :192], s, C, binding.EPI_F32_BIAS), "K a multiple of 128"),
-        (lambda: binding.gemm_i8(a, s, w[:384], s, C[:, :384], binding.EPI_F32_BIAS), "N a multiple of 256"),
-        (lambda: binding.gemm_i8(a[:, 8:136], s, w[:, :128], s, C, binding.EPI_F32_BIAS), "16-byte aligned"),
+        (lambda: binding.gemm_i8(a[:, :192], sa, w[:, :192], sw, C, binding.EPI_F32_BIAS), "K a multiple of 128"),
+        (lambda: binding.gemm_i8(a, sa, w[:384], sw[:384], C[:, :384], binding.EPI_F32_BIAS), "N a multiple of 256"),
+        (lambda: binding.gemm_i8(a[:, 8:136], sa, w[:, :128], sw, C, binding.EPI_F32_BIAS), "16-byte aligned"),
     ]
     for fn, msg in bad:
         with pytest.raises(binding.ZimgError) as ei:
