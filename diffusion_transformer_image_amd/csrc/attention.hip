@@ -10,9 +10,10 @@
 //
 // Workgroup = 4 waves = 128 queries of one head; each wave owns 32 queries.
 // Keys stream through LDS in tiles of 64 (K as [key][128], V as the
-// transposed [128][key] tile read from vT) by direct global->LDS loads into
-// double buffers; scores of the next tile are computed while the current
-// tile's softmax runs, so matrix-core and vector work overlap.
+// transposed [128][key] tile read from vT) by direct global->LDS loads, K
+// into three buffers (loaded three tiles ahead) and V^T into two; scores of
+// the next tile are computed while the current tile's softmax runs, so
+// matrix-core and vector work overlap.
 //
 // Orientation.  Scores are computed transposed, S^T = K Q^T, with the MFMA
 // A operand = 32 keys and B operand = 32 queries, so every lane holds 16
@@ -56,9 +57,13 @@ ZI_DEV float pair_sum(float v) {
 }
 
 __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
-  // K tiles [64 keys][128] and V^T tiles [128][64 keys], two of each
+  // K tiles [64 keys][128], three (tile t in K<t % 3>), and V^T tiles
+  // [128][64 keys], two (tile t in V<t % 2>): 80 KB, two workgroups per CU.
+  // Separate arrays, so the compiler can see that a load into one buffer
+  // never aliases reads of another (and waits only for the loads it must).
   __shared__ __attribute__((aligned(16))) bf16_t K0[KTILE * HD];
   __shared__ __attribute__((aligned(16))) bf16_t K1[KTILE * HD];
+  __shared__ __attribute__((aligned(16))) bf16_t K2[KTILE * HD];
   __shared__ __attribute__((aligned(16))) bf16_t V0[HD * KTILE];
   __shared__ __attribute__((aligned(16))) bf16_t V1[HD * KTILE];
 
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   const AttnSeg sg = a.segs[it.seg];
   const int D = a.H * HD;
   const int64_t ld = 3 * (int64_t)D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int swk = lrow & 15;        // K rows are 256 B: 16 rows per lane group on distinct banks
   const int swv = (lrow >> 1) & 7;  // V^T rows are 128 B: two rows per 256-byte bank line
@@ -272,31 +277,64 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     asm volatile("" : "+v"(lp[0]), "+v"(lp[1]), "+v"(lp[2]), "+v"(lp[3]));
   };
 
-  // The tile count is padded to an even number (>= 2) with an empty tile: its
-  // K is not loaded and every score is masked (selected to -inf), so its
-  // weights are exactly zero, and its V is a copy of a real tile.  The loop
-  // body is then the same for every pair of tiles, with no tail.  Indexes j
-  // are relative to the unit's first tile tb.
+  // The tile count is padded to an even number (>= 2) with an empty tile
+  // whose scores are all masked (selected to -inf), so its weights are
+  // exactly zero; the loop body is then the same for every pair of tiles,
+  // with no tail.  Indexes j are relative to the unit's first tile tb; loads
+  // of tiles past the range fetch the last real tile instead (into buffers
+  // no one reads), so every half issues the same loads.
+  //
+  // Loads run ahead: the half that computes the scores of tile j+1 and the
+  // PV product of tile j issues V(j+1) and then K(j+3).  Its closing barrier
+  // waits for all but the last four loads of each wave (vmcnt(4): K(j+3) may
+  // stay in flight), so a K tile has two halves to arrive and a V tile one.
   const int Tp = tn + (tn & 1);
   auto nvalid = [&](int j) { return j < tn ? tile_valid(tb + j) : 0; };
-  dma_k(tb, K0);
-  dma_v(tb, V0);
-  if (1 < tn) dma_k(tb + 1, K1);
-  dma_barrier();
+  auto clamp_t = [&](int j) { return tb + min(j, tn - 1); };
+  // All but this wave's newest 4 loads have landed and its LDS reads are
+  // done, then all waves meet.  Not __syncthreads(): its fence would also
+  // wait for the newest loads (it covers every outstanding load into LDS).
+  // The wait is the s_waitcnt builtin (vmcnt 4, lgkmcnt 0, expcnt off), so
+  // the compiler knows which loads have landed; the empty asm statements
+  // keep memory accesses from moving across the barrier.
+  auto load_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0074);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // one pair of halves (tiles j, j+1): the K buffers of tiles j+1, j+2 and
+  // the ones tiles j+3, j+4 are loaded into
+  auto pair = [&](int j, bf16_t* kq1, bf16_t* kq2, bf16_t* kl3, bf16_t* kl4, f32x16* sa, f32x16* sb) {
+    load_barrier();  // V(j), K(j+1) landed; everyone is done with K(j) and V(j-1)
+    dma_v(clamp_t(j + 1), V1);
+    dma_k(clamp_t(j + 3), kl3);
+    half(kq1, V0, sa, sb, nvalid(j));
+    load_barrier();  // V(j+1), K(j+2) landed; everyone is done with K(j+1) and V(j)
+    dma_v(clamp_t(j + 2), V0);
+    dma_k(clamp_t(j + 4), kl4);
+    half(kq2, V1, sb, sa, nvalid(j + 1));  // j + 1 == tn: the padding tile, fully masked
+  };
+  dma_k(clamp_t(0), K0);
+  dma_v(clamp_t(0), V0);
+  dma_k(clamp_t(1), K1);
+  dma_k(clamp_t(2), K2);
+  load_barrier();  // K(0), V(0), K(1)
   f32x16 sc[2], sn[2];
   qk(K0, sc);
-  for (int j = 0; j < Tp; j += 2) {
-    dma_barrier();  // K(j+1), V(j) landed; everyone is done with K(j) and V(j-1)
-    if (j + 2 < tn) dma_k(tb + j + 2, K0);
-    // V of tile j+1; for the padding tile (j + 1 == tn) the last real tile, so
-    // that its zero weights multiply finite values
-    dma_v(tb + min(j + 1, tn - 1), V1);
-    half(K1, V0, sc, sn, nvalid(j));
-    dma_barrier();
-    if (j + 3 < tn) dma_k(tb + j + 3, K1);
-    if (j + 2 < tn) dma_v(tb + j + 2, V0);
-    half(K0, V1, sn, sc, nvalid(j + 1));  // j + 1 == tn: the padding tile, fully masked
+  // pairs cycle through the three K-buffer assignments (j = 0, 2, 4 mod 6)
+  int j = 0;
+  for (; j + 6 <= Tp; j += 6) {
+    pair(j, K1, K2, K0, K1, sc, sn);
+    pair(j + 2, K0, K1, K2, K0, sc, sn);
+    pair(j + 4, K2, K0, K1, K2, sc, sn);
   }
+  if (j < Tp) {
+    pair(j, K1, K2, K0, K1, sc, sn);
+    if (j + 2 < Tp) pair(j + 2, K0, K1, K2, K0, sc, sn);
+  }
+  // no load may still be writing this workgroup's LDS when it ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   const float l = pair_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
   if (qi < it.nq && unit >= 0) {
