@@ -13,9 +13,11 @@
 //
 // Workgroup tile BM x BN, K-step 64, 512 threads = 8 waves (2 waves per
 // SIMD, so one wave's MFMAs cover the other's memory waits).  Operands go
-// global -> LDS directly (global_load_lds_dwordx4, no register staging) into
-// a two-stage ring: the next K-step's loads are issued early in the current
-// one, and one barrier per K-step publishes them.  LDS rows are
+// global -> LDS directly (global_load_lds_dwordx4, no register staging),
+// A into two stage buffers and W into three: early in each K-step the next
+// stage of A and the stage after next of W are issued, and one barrier per
+// K-step publishes a stage, waiting for all but the newest W loads.  LDS
+// rows are
 // 128 B (64 bf16); the 16-byte chunk c of row r
 // is stored at position c ^ ((r >> 1) & 7): the LDS serves 16 lanes x 16 B
 // per cycle, and with two rows per 256-byte bank line this makes the 16
@@ -30,6 +32,8 @@
 // ("Z-Image" (AI Toolkit docs), Architecture: QK RMSNorm and 3D RoPE).
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace zimg {
 namespace {
@@ -344,12 +348,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   constexpr int NB = BN * 8 / 64 / NW;
   static_assert(NA >= 1 && NB >= 1, "tile too small for 8 waves");
 
-  // two stages in separate arrays, so the compiler can see that loads into
-  // one stage never alias reads of the other
+  // A in two stage buffers (stage k in As<k % 2>), W in three (Bs<k % 3>),
+  // separate arrays, so the compiler can see that loads into one buffer
+  // never alias reads of another
   __shared__ __attribute__((aligned(16))) bf16_t As0[BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t Bs0[BN * BK];
   __shared__ __attribute__((aligned(16))) bf16_t As1[BM * BK];
   __shared__ __attribute__((aligned(16))) bf16_t Bs1[BN * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs2[BN * BK];
 
   // Work unit -> tile.  The first full_tiles units are whole tiles; each of
   // the remaining (total - full_tiles) tiles is split into nsplit K-ranges.
@@ -391,12 +397,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
     const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
     b_off[i] = (uint32_t)((min(n0 + row, N - 1) - n0) * ldw * 2 + lc * 16);
   }
-  auto issue = [&](int kt, bf16_t* as, bf16_t* bs) {
+  auto issue_a = [&](int kt, bf16_t* as) {
     const char* ak = a_base + (int64_t)kt * (BK * 2);
-    const char* bk = b_base + (int64_t)kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < NA; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(ak + a_off[i]), LDS_PTR(as + (i * NW + wid) * 512), 16, 0, 0);
+  };
+  auto issue_b = [&](int kt, bf16_t* bs) {
+    const char* bk = b_base + (int64_t)kt * (BK * 2);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(bk + b_off[i]), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
@@ -444,15 +452,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   // One K-step, entered with the operands of its first k16 step in set 0:
   // the MFMAs of the previous K-step's last k16 step (held back, operands in
   // set 1; they cover the latency of the set-0 reads issued just before),
-  // the next stage's loads, then three k16 steps whose MFMAs are interleaved
-  // one-for-one with the operand reads of the step after (the scheduling
-  // barriers pin that order).  The fourth k16 step's MFMAs are held back
-  // past the barrier that ends the K-step, behind the next stage's first
-  // operand reads.
-  auto step = [&](const bf16_t* as, const bf16_t* bs, bool prev_tail, bool do_issue, int kt_next, bf16_t* nas,
-                  bf16_t* nbs) {
+  // the loads of A one stage ahead and of W two stages ahead, then three
+  // k16 steps whose MFMAs are interleaved one-for-one with the operand reads
+  // of the step after (the scheduling barriers pin that order).  The fourth
+  // k16 step's MFMAs are held back past the barrier that ends the K-step,
+  // behind the next stage's first operand reads.
+  auto step = [&](const bf16_t* as, const bf16_t* bs, bool prev_tail, bool do_issue, int kt_a, bf16_t* nas,
+                  int kt_b, bf16_t* nbs) {
     if (prev_tail) mfmas(1);
-    if (do_issue) issue(kt_next, nas, nbs);
+    if (do_issue) {
+      issue_a(kt_a, nas);
+      issue_b(kt_b, nbs);
+    }
     __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);  // DS reads of the first k16 step (before the call)
     if (prev_tail) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);  // held-back MFMAs
     __builtin_amdgcn_sched_group_barrier(0x020, NA + NB, 0);  // VMEM (the loads above)
@@ -463,33 +474,72 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
       pin_pairs();
     }
   };
+  // The barrier that ends a K-step: all of this wave's loads but the newest
+  // NB (W two stages ahead) have landed and its LDS reads are done, then all
+  // waves meet.  Not __syncthreads(): its fence would also wait for the
+  // newest loads.  The wait is the s_waitcnt builtin (vmcnt NB, lgkmcnt 0,
+  // expcnt off), so the compiler knows which loads have landed; the empty
+  // asm statements keep memory accesses from moving across the barrier.
+  static_assert(NB <= 15, "vmcnt field");
+  auto stage_barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070 | NB);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   const int KTALL = K / BK;
   const int kt0 = is_split ? (int)((int64_t)chunk * KTALL / nsplit) : 0;
   const int KT = is_split ? (int)((int64_t)(chunk + 1) * KTALL / nsplit) : KTALL;
-  // K-steps alternate between the two buffers; every step except a lone
-  // last one issues loads, so the loop body has no branch that would keep
-  // them from interleaving with the MFMAs (where no stage is left to load,
-  // the step reloads its own stage into the free buffer: waited for by the
-  // next barrier, never read).
-  issue(kt0, As0, Bs0);
-  dma_barrier();
+  const int n = KT - kt0;
+  auto clamp_k = [&](int s) { return kt0 + min(s, n - 1); };
+  auto abuf = [&](auto r) -> bf16_t* {
+    if constexpr (decltype(r)::value % 2 == 0) return As0; else return As1;
+  };
+  auto bbuf = [&](auto r) -> bf16_t* {
+    if constexpr (decltype(r)::value % 3 == 0) return Bs0;
+    else if constexpr (decltype(r)::value % 3 == 1) return Bs1;
+    else return Bs2;
+  };
+  // K-step s of the unit (stage kt0 + s) uses As<s % 2> and Bs<s % 3>; the
+  // buffers are compile-time constants of s mod 6, so the steps run in
+  // groups of six, then a tail of up to five.  Every step issues loads (of
+  // the last stage again where none is left: into a free buffer, never read),
+  // so the loop body has no branch that would keep them from interleaving
+  // with the MFMAs; the loads are drained before the epilogue.
+  auto kstep = [&](auto r, int s) {
+    constexpr int R = decltype(r)::value;
+    using C0 = std::integral_constant<int, R>;
+    using C1 = std::integral_constant<int, R + 1>;
+    using C2 = std::integral_constant<int, R + 2>;
+    step(abuf(C0{}), bbuf(C0{}), true, true, clamp_k(s + 1), abuf(C1{}), clamp_k(s + 2), bbuf(C2{}));
+    stage_barrier();
+    frags(abuf(C1{}), bbuf(C1{}), 0, 0);
+  };
+  issue_a(kt0, As0);
+  issue_b(kt0, Bs0);
+  issue_b(clamp_k(1), Bs1);
+  stage_barrier();  // A and W of stage kt0
   frags(As0, Bs0, 0, 0);
-  step(As0, Bs0, false, true, kt0 + 1 < KT ? kt0 + 1 : kt0, As1, Bs1);
-  dma_barrier();
-  int kt = kt0 + 1;
-  for (; kt + 2 <= KT; kt += 2) {
-    frags(As1, Bs1, 0, 0);
-    step(As1, Bs1, true, true, kt + 1, As0, Bs0);
-    dma_barrier();
-    frags(As0, Bs0, 0, 0);
-    step(As0, Bs0, true, true, kt + 2 < KT ? kt + 2 : kt + 1, As1, Bs1);
-    dma_barrier();
+  // the first step has no held-back MFMAs before it
+  step(As0, Bs0, false, true, clamp_k(1), As1, clamp_k(2), Bs2);
+  stage_barrier();
+  frags(As1, Bs1, 0, 0);
+  int s = 1;
+  for (; s + 6 <= n; s += 6) {
+    kstep(std::integral_constant<int, 1>{}, s);
+    kstep(std::integral_constant<int, 2>{}, s + 1);
+    kstep(std::integral_constant<int, 3>{}, s + 2);
+    kstep(std::integral_constant<int, 4>{}, s + 3);
+    kstep(std::integral_constant<int, 5>{}, s + 4);
+    kstep(std::integral_constant<int, 6>{}, s + 5);
   }
-  if (kt < KT) {
-    frags(As1, Bs1, 0, 0);
-    step(As1, Bs1, true, false, 0, As0, Bs0);
-  }
+  if (s < n) kstep(std::integral_constant<int, 1>{}, s);
+  if (s + 1 < n) kstep(std::integral_constant<int, 2>{}, s + 1);
+  if (s + 2 < n) kstep(std::integral_constant<int, 3>{}, s + 2);
+  if (s + 3 < n) kstep(std::integral_constant<int, 4>{}, s + 3);
+  if (s + 4 < n) kstep(std::integral_constant<int, 5>{}, s + 4);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS the epilogue reuses
   mfmas(1);  // the last K-step's fourth k16 step
 
   if (is_split) {
@@ -737,10 +787,10 @@ int group_rows(int role, int tiles_n) {
 
 template <int BM, int BN, int WM, int WN, int EPI, int ROLE, bool I8>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
-  static_assert(2 * (BM + BN) * BK * 2 <= 160 * 1024, "LDS budget");
+  static_assert((2 * BM + 3 * BN) * BK * 2 <= 160 * 1024, "LDS budget");
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int T = tiles_m * tiles_n;
-  constexpr int LDS_BYTES = 2 * (BM + BN) * BK * 2;
+  constexpr int LDS_BYTES = (2 * BM + 3 * BN) * BK * 2;
   constexpr int U = I8 ? 2 : 1;  // elements per bf16-sized unit
   const int K = g.K / U;
   GemmSplit sp = g.split;
