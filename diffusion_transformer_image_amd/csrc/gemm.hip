@@ -777,10 +777,10 @@ int choose_split(int T, int KT, int tile_bytes, const GemmSplit& sp) {
 // and was chosen by measuring the forward with each value.
 int group_rows(int role, int tiles_n) {
   switch (role) {
-    case ROLE_QKV: return 3;
-    case ROLE_W13: return 2;
+    case ROLE_QKV: return 4;
+    case ROLE_W13: return 3;
     case ROLE_OUT:
-    case ROLE_W2: return 6;
+    case ROLE_W2: return 8;
     default: return tiles_n >= 32 ? 3 : 6;
   }
 }
