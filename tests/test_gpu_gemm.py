@@ -48,6 +48,24 @@ def test_gemm_bf16_out(M, N, K):
     assert np.max(np.abs(got - ref)) <= 8e-3 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("n_steps", [2, 3, 4, 6, 7, 8, 12, 13, 19])
+def test_gemm_k_step_counts(n_steps):
+    """Every count of 64-wide K-steps around the kernel's six-step groups
+    (W rotates through three LDS buffers, A through two): a lone first step,
+    zero to three full groups, and tails of one to five steps, each against
+    the float64 product with the fp32 epilogue's tight bar."""
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    M, N, K = 300, 256, 64 * n_steps
+    A, W = _operands(M, N, K, 11 * n_steps)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    binding.gemm_bf16(_dev_bf16(A), _dev_bf16(W), C, binding.EPI_F32_BIAS)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    ref = A.astype(np.float64) @ W.astype(np.float64).T
+    assert helpers.rel_l2(got, ref) <= 2e-5
+
+
 @pytest.mark.parametrize("M,N,K", [(257, 64, 3840), (4096, 3840, 64), (33, 256, 2560)])
 def test_gemm_f32_bias(M, N, K):
     torch = _torch()
