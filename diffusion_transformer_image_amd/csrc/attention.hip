@@ -297,6 +297,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // The wait is the s_waitcnt builtin (vmcnt 4, lgkmcnt 0, expcnt off), so
   // the compiler knows which loads have landed; the empty asm statements
   // keep memory accesses from moving across the barrier.
+  // a K or V^T tile is 16 KB: 4 loads of 1 KB per wave of the 4
+  static_assert(KTILE * HD * 2 == 4 * 4 * 1024, "load_barrier's vmcnt(4) counts one tile's loads per wave");
   auto load_barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0074);
