@@ -81,6 +81,22 @@ ZI_DEV void dma_barrier() {
   __syncthreads();
 }
 
+// v from lane (lane ^ M) of the same 16-lane row, by DPP moves: quad
+// permutations for 1 and 2 (and 3), a half-row mirror (lane ^ 7) after a
+// quad xor 3 for 4, a row rotation by 8 for 8 (every source lane is inside
+// the row, so bound_ctrl never applies)
+template <int CTRL>
+ZI_DEV float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <int M>
+ZI_DEV float lane_xor(float v) {
+  if constexpr (M == 1) return dpp_mov<0xb1>(v);                 // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_mov<0x4e>(v);            // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_mov<0x141>(dpp_mov<0x1b>(v));  // quad [3,2,1,0], half-row mirror
+  else return dpp_mov<0x128>(v);                                 // row_ror:8
+}
+
 ZI_DEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -167,11 +167,11 @@ ZI_DEV void qk_rope_unit(const u32x4& x, int k, const float (&wv)[8], float eps,
     ss = fmaf(a, a, ss);
     ss = fmaf(b, b, ss);
   }
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
-  ss += __shfl_xor(ss, 4, 64);
-  ss += __shfl_xor(ss, 8, 64);
-  const float inv = 1.0f / sqrtf(ss * (1.0f / 128.0f) + eps);
+  ss += lane_xor<1>(ss);  // sums over the 16 lanes, in registers (DPP)
+  ss += lane_xor<2>(ss);
+  ss += lane_xor<4>(ss);
+  ss += lane_xor<8>(ss);
+  const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / 128.0f) + eps);  // hardware 1/sqrt (about 1 ulp)
   const float4 cc = *reinterpret_cast<const float4*>(cos_row + k * 4);
   const float4 sc = *reinterpret_cast<const float4*>(sin_row + k * 4);
   const float cv[4] = {cc.x, cc.y, cc.z, cc.w}, sv[4] = {sc.x, sc.y, sc.z, sc.w};

@@ -207,21 +207,6 @@ __global__ __launch_bounds__(256) void rows_rmsnorm_kernel(const void* x, const 
 // block, lane stride 1, 2, 4, 8); K % 128 == 0.
 constexpr int QMAXC = 8;
 
-// v from lane (lane ^ M) of the same 16-lane row, by DPP moves: quad
-// permutations for 1 and 2 (and 3), a half-row mirror (lane ^ 7) after a
-// quad xor 3 for 4, a row rotation by 8 for 8 (every source lane is inside
-// the row, so bound_ctrl never applies)
-template <int CTRL>
-ZI_DEV float dpp_mov(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
-}
-template <int M>
-ZI_DEV float lane_xor(float v) {
-  if constexpr (M == 1) return dpp_mov<0xb1>(v);                 // quad_perm [1,0,3,2]
-  else if constexpr (M == 2) return dpp_mov<0x4e>(v);            // quad_perm [2,3,0,1]
-  else if constexpr (M == 4) return dpp_mov<0x141>(dpp_mov<0x1b>(v));  // quad [3,2,1,0], half-row mirror
-  else return dpp_mov<0x128>(v);                                 // row_ror:8
-}
 // one cross-lane butterfly stage (lane stride M) on all chunks a thread holds
 // (slots i >= ni hold no chunk of any thread; ni is uniform)
 // The lower lane of a pair keeps a + b, the upper a - b (a: the lower's
