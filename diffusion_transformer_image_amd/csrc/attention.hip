@@ -370,22 +370,28 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 
 // Merge the chunks of one split (item, head) pair: with M the largest chunk
 // reference max, weight w_c = 2^(m_c - M); O = sum_c w_c O_c / sum_c w_c l_c,
-// summed in chunk order.
+// summed in chunk order.  One workgroup per (pair, slice of CQ queries), so
+// the merge spreads over many CUs; 16 lanes per query, 8 dims each, with all
+// chunks' loads in flight together.
+constexpr int CQ = 16;
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
-  __shared__ float wt[MAX_SPLIT][128];
+  __shared__ float wt[MAX_SPLIT][CQ];
   const int n_rest = a.n_items * a.H - a.n_full;
   const int p = blockIdx.x;
   const int lid = a.n_full + p;
   const int h = lid / a.n_items;
   const AttnItem it = a.items[lid - h * a.n_items];
+  const int qb = blockIdx.y * CQ;
+  if (qb >= it.nq) return;  // the whole workgroup: a slice past the item's queries
   const float* ml = a.part + (int64_t)n_rest * a.split * (128 * HD);
   const int tid = threadIdx.x;
-  if (tid < it.nq) {
+  if (tid < CQ && qb + tid < it.nq) {
+    const int q = qb + tid;
     float M = -INFINITY;
-    for (int c = 0; c < a.split; ++c) M = fmaxf(M, ml[((int64_t)(c * n_rest + p) * 128 + tid) * 2]);
+    for (int c = 0; c < a.split; ++c) M = fmaxf(M, ml[((int64_t)(c * n_rest + p) * 128 + q) * 2]);
     float L = 0.f;
     for (int c = 0; c < a.split; ++c) {
-      const float* v = ml + ((int64_t)(c * n_rest + p) * 128 + tid) * 2;
+      const float* v = ml + ((int64_t)(c * n_rest + p) * 128 + q) * 2;
       const float w = exp2f(v[0] - M);
       wt[c][tid] = w;
       L += w * v[1];
@@ -394,31 +400,28 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
     for (int c = 0; c < a.split; ++c) wt[c][tid] *= inv;
   }
   __syncthreads();
-  const int D = a.H * HD;
-  // thread: float4 number tid + 256 k (k < 16) of the 128 x 128 tile, i.e.
-  // query (tid >> 5) + 8 k, dims (tid & 31) * 4 .. +3; chunk-outer so that a
-  // chunk's 16 loads are in flight together (queries past nq combine stale
-  // workspace values with weight 0 and are never stored)
-  const int d = (tid & 31) * 4, q0 = tid >> 5;
-  f32x4 acc[16];
+  const int ql = tid >> 4, q = qb + ql, d = (tid & 15) * 8;
+  if (q >= it.nq) return;
+  const float* src = a.part + (int64_t)p * (128 * HD) + q * HD + d;
+  const int64_t cstride = (int64_t)n_rest * (128 * HD);  // chunk c of pair p is unit c * n_rest + p
+  f32x4 v0[MAX_SPLIT], v1[MAX_SPLIT];
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc[k] = f32x4{};
-  for (int c = 0; c < a.split; ++c) {
-    const float* src = a.part + (int64_t)(c * n_rest + p) * (128 * HD) + q0 * HD + d;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int q = q0 + 8 * k;
-      const float w = q < it.nq ? wt[c][q] : 0.f;
-      acc[k] += w * *reinterpret_cast<const f32x4*>(src + 8 * k * HD);
+  for (int c = 0; c < MAX_SPLIT; ++c)
+    if (c < a.split) {
+      v0[c] = *reinterpret_cast<const f32x4*>(src + c * cstride);
+      v1[c] = *reinterpret_cast<const f32x4*>(src + c * cstride + 4);
     }
-  }
+  f32x4 acc0 = {}, acc1 = {};
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int q = q0 + 8 * k;
-    if (q >= it.nq) continue;
-    u32x2 u = {pack2bf(acc[k][0], acc[k][1]), pack2bf(acc[k][2], acc[k][3])};
-    *reinterpret_cast<u32x2*>(a.out + (int64_t)(it.q0 + q) * D + h * HD + d) = u;
-  }
+  for (int c = 0; c < MAX_SPLIT; ++c)
+    if (c < a.split) {
+      const float w = wt[c][ql];
+      acc0 += w * v0[c];
+      acc1 += w * v1[c];
+    }
+  const u32x4 u = {pack2bf(acc0[0], acc0[1]), pack2bf(acc0[2], acc0[3]), pack2bf(acc1[0], acc1[1]),
+                   pack2bf(acc1[2], acc1[3])};
+  *reinterpret_cast<u32x4*>(a.out + (int64_t)(it.q0 + q) * (a.H * HD) + h * HD + d) = u;
 }
 
 }  // namespace
@@ -430,7 +433,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n_full < 0 || n_rest < 0 || (n_rest > 0 && (a.split < 2 || a.split > MAX_SPLIT || !a.part)))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(attention_kernel, dim3(a.n_full + n_rest * (n_rest > 0 ? a.split : 0)), dim3(256), 0, s, a);
-  if (n_rest > 0) hipLaunchKernelGGL(attention_combine_kernel, dim3(n_rest), dim3(256), 0, s, a);
+  if (n_rest > 0) hipLaunchKernelGGL(attention_combine_kernel, dim3(n_rest, 128 / CQ), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -586,7 +586,7 @@ template <int BM, int BN, int WM, int WN, int EPI, bool I8>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, EpiArgs ep, int tiles_m, int tiles_n,
                                                           int full_tiles, int nsplit, const float* __restrict__ ws,
                                                           int gm) {
-  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  constexpr int WTM = BM / WM, WTN = BN / WN, TN = WTN / 32;
   constexpr int TILE_F = BM * BN;
   constexpr int SLOTS = (EPI == EPI_SWIGLU) ? TILE_F / 2 : TILE_F;  // outputs per tile
   constexpr int PER_WG = 256 * RED_PER_THREAD;
@@ -670,7 +670,7 @@ __global__ __launch_bounds__(256) void gemm_qkv_reduce_kernel(int M, EpiArgs ep,
                                                               int full_tiles, int nsplit, const float* __restrict__ ws,
                                                               int gm) {
   static_assert(BM == 256 && BN == 256 && WM == 2 && WN == 4, "QKV epilogue tiling");
-  constexpr int TM = 4, TN = 2, TILE_F = BM * BN;
+  constexpr int TN = 2, TILE_F = BM * BN;
   __shared__ __attribute__((aligned(16))) bf16_t st[32 * 256];
   const int tail_idx = blockIdx.x >> 3, slice = blockIdx.x & 7;
   const int wm = slice >> 2, i = slice & 3;  // rows wm*128 + i*32 .. +31 of the tile
