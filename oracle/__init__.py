@@ -29,7 +29,12 @@ Parity status per function (what pins it; see tests/test_oracle_*.py):
   rope tables / apply_rope pinned: closed-form entries, norm, relativity
   attention                pinned: brute-force loops, torch SDPA
   swiglu ffn               pinned: exact 1/64 compensation, hand formula
-  block wiring             pinned: zero-gate identity, unmodulated reduction
+  block wiring             pinned: zero-gate identity, unmodulated reduction,
+                           one modulated block written out by hand (non-zero
+                           tanh gates, QK-RMSNorm before RoPE), with planted
+                           mutants that the pin rejects
+  timestep MLP             pinned: by-hand loops and torch Linear/SiLU
+  caption embedder         pinned: by-hand loops and torch rms_norm/linear
   patchify / unpatchify    pinned: brute-force index loops, token counts
   sampler schedule         pinned: exact rational values of the closed form
   timestep embedding       pinned: closed-form entries (constants themselves
