@@ -79,8 +79,8 @@ SIGNATURES = {
     "zimg_dit_manifest_size": (_I32, [ctypes.POINTER(Config), _I32P]),
     "zimg_dit_manifest_entry": (_I32, [ctypes.POINTER(Config), _I32, ctypes.POINTER(ctypes.c_char_p), _I32P,
                                        ctypes.POINTER(ctypes.c_int64)]),
-    "zimg_dit_create": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(Tensor), _I32, ctypes.POINTER(_P)]),
-    "zimg_dit_alloc": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(_P)]),
+    "zimg_dit_create": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(Tensor), _I32, _P, ctypes.POINTER(_P)]),
+    "zimg_dit_alloc": (_I32, [ctypes.POINTER(Config), _P, ctypes.POINTER(_P)]),
     "zimg_dit_set_weight": (_I32, [_P, ctypes.POINTER(Tensor)]),
     "zimg_dit_finalize": (_I32, [_P]),
     "zimg_dit_forward": (_I32, [_P, _P, _I32, _I32, _I32, _P, _I32, _I32P, _F32P, _P, _P]),
@@ -97,6 +97,8 @@ SIGNATURES = {
     "zimg_gemm_i8": (_I32, [_P, _I64, _P, _P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
     "zimg_quantize_rows": (_I32, [_P, _I32, _I64, _P, _I64, _P, _I32, _I32, _I32, _P]),
     "zimg_euler_step": (_I32, [_P, _P, ctypes.c_float, _I64, _P]),
+    "zimg_flowmatch_schedule": (_I32, [_I32, ctypes.c_double, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double)]),
     "zimg_cfg_euler_step": (_I32, [_P, _P, _P, ctypes.c_float, ctypes.c_float, _I64, _P]),
     "zimg_dit_profile": (_I32, [_P, _I32]),
     "zimg_dit_profile_read": (_I32, [_P, ctypes.POINTER(KernelStat), _I32, _I32P]),
@@ -213,6 +215,28 @@ def _f32():
     return (torch.float32,)
 
 
+def _per_sample(caption_lens, t, B):
+    """Host arrays of one caption length and one model time per sample; the
+    library reads exactly B of each, so shorter (or longer) sequences are
+    refused here."""
+    lens = np.ascontiguousarray(caption_lens, dtype=np.int32).reshape(-1)
+    tt = np.ascontiguousarray(t, dtype=np.float32).reshape(-1)
+    if lens.size != B:
+        raise ValueError(f"caption_lens: {B} lengths required (one per sample), got {lens.size}")
+    if tt.size != B:
+        raise ValueError(f"t: {B} model times required (one per sample), got {tt.size}")
+    return lens, tt
+
+
+def _check_captions(caption_feats, lens, cap_dim):
+    """Packed caption rows: cap_feat_dim wide and at least as many rows as
+    the lengths add up to (the library reads exactly that many)."""
+    need = int(np.clip(lens.astype(np.int64), 0, None).sum())
+    if caption_feats.shape[1] != cap_dim or caption_feats.shape[0] < need:
+        raise ValueError(f"caption_feats must be [>= {need}, {cap_dim}] (the captions packed back to back), "
+                         f"got {list(caption_feats.shape)}")
+
+
 def _f32_bf16():
     import torch
     return (torch.float32, torch.bfloat16)
@@ -221,11 +245,12 @@ def _f32_bf16():
 class DiT:
     """Handle of one engine instance (device weights + workspace)."""
 
-    def __init__(self, cfg, weights):
-        """``weights``: iterable of (name, numpy array) or a mapping."""
+    def __init__(self, cfg, weights, stream=None):
+        """``weights``: iterable of (name, numpy array) or a mapping.  The
+        set-up work runs on ``stream`` (default: torch's current stream)."""
         self.cfg = cfg
         self._h = ctypes.c_void_p()
-        _check(lib().zimg_dit_alloc(ctypes.byref(cfg), ctypes.byref(self._h)))
+        _check(lib().zimg_dit_alloc(ctypes.byref(cfg), _stream(stream), ctypes.byref(self._h)))
         try:
             items = weights.items() if hasattr(weights, "items") else weights
             for name, arr in items:
@@ -264,8 +289,10 @@ class DiT:
         if out.shape != latent.shape:
             raise ValueError("out must have the latent's shape")
         B, C, Hl, Wl = latent.shape
-        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
-        tt = np.ascontiguousarray(t, dtype=np.float32)
+        if C != self.cfg.in_channels:
+            raise ValueError(f"latent: {self.cfg.in_channels} channels required, got {C}")
+        lens, tt = _per_sample(caption_lens, t, B)
+        _check_captions(caption_feats, lens, self.cfg.cap_feat_dim)
         cap_dt = ZIMG_BF16 if caption_feats.dtype == torch.bfloat16 else ZIMG_F32
         _check(lib().zimg_dit_forward(self._h, _ptr(latent), B, Hl, Wl, _ptr(caption_feats), cap_dt,
                                       lens.ctypes.data_as(_I32P), tt.ctypes.data_as(_F32P), _ptr(out),
@@ -284,13 +311,18 @@ class DiT:
         for x, o in zip(latents, outs):
             _want(x, "latents", _f32(), contiguous=True)
             _want(o, "outs", _f32(), contiguous=True)
-            if tuple(o.shape[-3:]) != tuple(x.shape[-3:]):
+            shp = tuple(x.shape)
+            if len(shp) == 4 and shp[0] == 1:
+                shp = shp[1:]
+            if len(shp) != 3 or shp[0] != self.cfg.in_channels:
+                raise ValueError(f"latents: [{self.cfg.in_channels}, Hl, Wl] per sample required, got {list(x.shape)}")
+            if o.numel() != x.numel() or tuple(o.shape[-3:]) != tuple(x.shape[-3:]):
                 raise ValueError("latents and outs: contiguous fp32 tensors of matching shapes")
         _want(caption_feats, "caption_feats", _f32_bf16(), 2, contiguous=True)
+        lens, tt = _per_sample(caption_lens, t, B)
+        _check_captions(caption_feats, lens, self.cfg.cap_feat_dim)
         lp = (ctypes.c_void_p * B)(*[x.data_ptr() for x in latents])
         op = (ctypes.c_void_p * B)(*[o.data_ptr() for o in outs])
-        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
-        tt = np.ascontiguousarray(t, dtype=np.float32)
         cap_dt = ZIMG_BF16 if caption_feats.dtype == torch.bfloat16 else ZIMG_F32
         _check(lib().zimg_dit_forward_varsize(self._h, lp, B, hl.ctypes.data_as(_I32P), wl.ctypes.data_as(_I32P),
                                               _ptr(caption_feats), cap_dt, lens.ctypes.data_as(_I32P),
@@ -298,9 +330,17 @@ class DiT:
         return outs
 
     def run_blocks(self, x, B, Hl, Wl, caption_lens, t, first, n, stream=None):
+        """Blocks [first, first + n) in place on the fp32 residual x (torch
+        CUDA, [S_total, hidden] in the engine's row layout)."""
         _want(x, "x", _f32(), contiguous=True)
-        lens = np.ascontiguousarray(caption_lens, dtype=np.int32)
-        tt = np.ascontiguousarray(t, dtype=np.float32)
+        lens, tt = _per_sample(caption_lens, t, B)
+        p = self.cfg.patch
+        if Hl % p or Wl % p or Hl <= 0 or Wl <= 0:
+            raise ValueError(f"Hl and Wl must be positive multiples of {p}, got {Hl} x {Wl}")
+        _, _, S = row_layout(B, (Hl // p) * (Wl // p), lens)
+        if x.numel() != S * self.cfg.hidden:
+            raise ValueError(f"x: {S} x {self.cfg.hidden} values required (the row layout of this batch), "
+                             f"got {x.numel()}")
         _check(lib().zimg_dit_run_blocks(self._h, _ptr(x), B, Hl, Wl, lens.ctypes.data_as(_I32P),
                                          tt.ctypes.data_as(_F32P), first, n, _stream(stream)), self._h)
         return x
@@ -444,6 +484,16 @@ def cfg_euler_step(x, out_cond, out_uncond, guidance, dt, stream=None):
     _check(lib().zimg_cfg_euler_step(_ptr(x), _ptr(out_cond), _ptr(out_uncond), float(guidance), float(dt),
                                      x.numel(), _stream(stream)))
     return x
+
+
+def flowmatch_schedule(n_steps, shift):
+    """(sigma' [n_steps + 1] ending at 0, model times t [n_steps]) as float64
+    numpy arrays, computed by the library (zimg_flowmatch_schedule)."""
+    sig = np.zeros(max(int(n_steps), 0) + 1, np.float64)
+    t = np.zeros(max(int(n_steps), 1), np.float64)  # (the library refuses n_steps < 1)
+    dp = ctypes.POINTER(ctypes.c_double)
+    _check(lib().zimg_flowmatch_schedule(int(n_steps), float(shift), sig.ctypes.data_as(dp), t.ctypes.data_as(dp)))
+    return sig, t
 
 
 def euler_step(x, model_out, dt, stream=None):

@@ -51,3 +51,71 @@ def test_want_rules():
         binding._want(fake(torch.zeros((4, 16))[:, :8]), "x", (torch.float32,), 2, contiguous=True)
     # a row-sliced view (unit-stride rows, larger leading stride) is accepted without ``contiguous``
     binding._want(fake(torch.zeros((4, 16))[:, :8]), "x", (torch.float32,), 2)
+
+
+class _FakeCuda(torch.Tensor):
+    @property
+    def is_cuda(self):
+        return True
+
+
+def _fake(*shape, dtype=torch.float32):
+    return torch.zeros(shape, dtype=dtype).as_subclass(_FakeCuda)
+
+
+def _handle(**model):
+    """A DiT object without a native handle: every case below must be
+    refused by the binding before the library is called."""
+    d = binding.DiT.__new__(binding.DiT)
+    d.cfg = binding.config(max_batch=4, max_image_tokens=256, max_caption_tokens=64, **model)
+    d._h = None
+    return d
+
+
+def test_forward_shape_mismatches_are_refused():
+    d = _handle()
+    lat, out = _fake(2, 16, 8, 8), _fake(2, 16, 8, 8)
+    caps = _fake(10, 2560)
+    with pytest.raises(ValueError, match="channels"):
+        d.forward(_fake(2, 8, 8, 8), caps, [4, 6], [0.5, 0.5], _fake(2, 8, 8, 8))
+    with pytest.raises(ValueError, match="caption_lens"):
+        d.forward(lat, caps, [10], [0.5, 0.5], out)
+    with pytest.raises(ValueError, match="model times"):
+        d.forward(lat, caps, [4, 6], [0.5], out)
+    with pytest.raises(ValueError, match="caption_feats"):
+        d.forward(lat, _fake(9, 2560), [4, 6], [0.5, 0.5], out)
+    with pytest.raises(ValueError, match="caption_feats"):
+        d.forward(lat, _fake(2560), [4, 6], [0.5, 0.5], out)
+    with pytest.raises(ValueError, match="caption_feats"):
+        d.forward(lat, _fake(10, 2048), [4, 6], [0.5, 0.5], out)
+
+
+def test_forward_varsize_shape_mismatches_are_refused():
+    d = _handle()
+    lats = [_fake(16, 8, 8), _fake(16, 4, 6)]
+    outs = [_fake(16, 8, 8), _fake(16, 4, 6)]
+    caps = _fake(7, 2560)
+    with pytest.raises(ValueError, match="per sample"):
+        d.forward_varsize([_fake(8, 8, 8), lats[1]], caps, [3, 4], [0.1, 0.2], [_fake(8, 8, 8), outs[1]])
+    with pytest.raises(ValueError, match="matching shapes"):
+        d.forward_varsize(lats, caps, [3, 4], [0.1, 0.2], [outs[0], _fake(16, 4, 4)])
+    with pytest.raises(ValueError, match="caption_lens"):
+        d.forward_varsize(lats, caps, [7], [0.1, 0.2], outs)
+    with pytest.raises(ValueError, match="model times"):
+        d.forward_varsize(lats, caps, [3, 4], [0.1], outs)
+    with pytest.raises(ValueError, match="caption_feats"):
+        d.forward_varsize(lats, _fake(6, 2560), [3, 4], [0.1, 0.2], outs)
+
+
+def test_run_blocks_residual_size_is_checked():
+    d = _handle(n_layers=1, n_noise_refiner=0, n_context_refiner=0)
+    # one sample, 8x8 latent -> 16 image tokens, caption of 5 -> 16 + 16 rows
+    _, _, S = binding.row_layout(1, 16, [5])
+    with pytest.raises(ValueError, match="values required"):
+        d.run_blocks(_fake(S - 1, d.cfg.hidden), 1, 8, 8, [5], [0.5], 0, 1)
+    with pytest.raises(ValueError, match="caption_lens"):
+        d.run_blocks(_fake(S, d.cfg.hidden), 1, 8, 8, [5, 5], [0.5], 0, 1)
+    with pytest.raises(ValueError, match="model times"):
+        d.run_blocks(_fake(S, d.cfg.hidden), 1, 8, 8, [5], [], 0, 1)
+    with pytest.raises(ValueError, match="multiples"):
+        d.run_blocks(_fake(S, d.cfg.hidden), 1, 7, 8, [5], [0.5], 0, 1)

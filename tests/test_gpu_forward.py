@@ -95,9 +95,8 @@ def _compare_forward(model, wl_latent, lens, t, max_img, max_cap, seed=0):
                 g_prev, o_prev = got, want
             r, cs = helpers.assert_parity(got, want, f"sample {b} {p}")
             # what the block added, compared on its own (not diluted by the residual)
-            rb = helpers.rel_l2(got - gin, want - oin)
-            assert rb <= 3e-2, f"sample {b} {p}: branch rel-L2 {rb:.3e}"
-            report.append((b, p, r, cs, rb))
+            rb, rw = helpers.assert_branch(got, gin, want, oin, f"sample {b} {p}")
+            report.append((b, p, f"rel-L2 {r:.2e}", f"cos {cs:.7f}", f"branch {rb:.2e}", f"worst row {rw:.2e}"))
         helpers.assert_parity(out[b], ref, f"sample {b} final output")
     return report, dit
 
@@ -137,6 +136,16 @@ def test_forward_degenerate_geometries(latent, lens):
     print(rep[-1])
 
 
+# alone vs in batch with the default splits: the batch changes which GEMM
+# tiles are split along K (fp32 summation order) and which attention pairs
+# are split along keys; a split chunk rounds its probabilities to bf16
+# relative to its own running max, so those roundings differ from the
+# unsplit pair's, by about the bf16 step per weight.  With zero-mean values
+# that noise does not average out in the weighted sum, which puts the two
+# runs ~2e-3 apart after this 4-block model (measured 2.2e-3)
+SPLIT_ORDER_TOL = 5e-3
+
+
 @pytest.mark.parametrize("batch_invariant", [0, 1])
 def test_determinism_and_batch_independence(batch_invariant):
     """Two identical calls are bitwise equal.  A sample run alone matches its
@@ -162,7 +171,8 @@ def test_determinism_and_batch_independence(batch_invariant):
             assert torch.equal(ob[0], o1[b]), f"sample {b} alone vs in batch differ"
         else:
             r = helpers.rel_l2(ob[0].cpu().numpy(), o1[b].cpu().numpy())
-            assert r <= helpers.REL_L2_TOL, f"sample {b} alone vs in batch: rel-L2 {r:.3e}"
+            print(f"sample {b}: alone vs in batch rel-L2 {r:.3e}")
+            assert r <= SPLIT_ORDER_TOL, f"sample {b} alone vs in batch: rel-L2 {r:.3e}"
 
 
 def test_caption_bf16_input_matches_fp32():
@@ -182,7 +192,7 @@ def test_forward_argument_errors():
     from diffusion_transformer_image_amd import binding
     dit = _make_engine(SMALL, 1, 120, 77, seed=5)
     lat_d = torch.zeros((1, 16, 24, 20), device="cuda")
-    caps_d = torch.zeros((50, 2560), device="cuda")
+    caps_d = torch.zeros((200, 2560), device="cuda")  # rows for every case's lengths
     out = torch.empty_like(lat_d)
     def run(lat, lens, t):
         return dit.forward(lat, caps_d, lens, t, torch.empty_like(lat))
@@ -234,3 +244,40 @@ def test_weight_table_errors():
     assert ei.value.code == binding.ZIMG_EWEIGHT and "x_embedder.weight" in str(ei.value)
     # fp32 and bf16-bit inputs give the same engine
     binding.DiT(ecfg, W).close()
+
+
+def test_geometry_switches_reuse_cached_tables():
+    """Forwards that alternate between geometries (more of them than the
+    engine keeps tables for, so slots are evicted and rebuilt) give bitwise
+    the outputs of the first forward at each geometry, and the attention
+    plan follows the geometry of the latest call."""
+    torch = _torch()
+    dit = _make_engine(SMALL, 2, 120, 77, seed=6)
+    geos = [((1, 16, 24, 20), (50,)), ((2, 16, 24, 20), (50, 31)), ((1, 16, 16, 16), (20,)),
+            ((2, 16, 8, 12), (1, 77)), ((1, 16, 20, 24), (64,)), ((2, 16, 16, 16), (16, 17))]
+    inputs = [_inputs(shape, lens, seed=10 + i) for i, (shape, lens) in enumerate(geos)]
+
+    def run(i):
+        (shape, lens), (_, _, lat_d, caps_d) = geos[i], inputs[i]
+        out = torch.empty_like(lat_d)
+        dit.forward(lat_d, caps_d, lens, tuple(0.25 + 0.5 * b for b in range(len(lens))), out)
+        return out
+
+    first = {}
+    order = [0, 1, 0, 1, 2, 3, 4, 5, 0, 2, 1, 5, 5, 3]
+    outs = [run(i) for i in order]  # enqueued back to back, no synchronisation in between
+    torch.cuda.synchronize()
+    for i, o in zip(order, outs):
+        if i not in first:
+            first[i] = o
+        else:
+            assert torch.equal(o, first[i]), f"geometry {geos[i]} changed after switching"
+    plan_last = dit.attention_plan(2)
+    # a fresh engine at the last geometry makes the same plan
+    dit2 = _make_engine(SMALL, 2, 120, 77, seed=6)
+    lat_d, caps_d = inputs[order[-1]][2], inputs[order[-1]][3]
+    dit2.forward(lat_d, caps_d, geos[order[-1]][1], (0.25, 0.75), torch.empty_like(lat_d))
+    torch.cuda.synchronize()
+    assert dit2.attention_plan(2) == plan_last
+    dit.close()
+    dit2.close()
