@@ -302,6 +302,7 @@ struct zimg_dit {
   zimg_dit_config cfg{};
   std::string err;
   int device = 0;
+  hipStream_t setup = nullptr;  // the stream given at create: weight uploads, repacking, clears
   std::vector<ManifestEntry> manifest;
   std::vector<BlockSpec> blocks;
   std::vector<int> mod_index;  // per block, -1 if unmodulated
@@ -347,16 +348,34 @@ struct zimg_dit {
   float *normw = nullptr, *fold = nullptr;
   int32_t* mod_idx_d = nullptr;
   int64_t fold_stride = 0;
+  // Per-geometry tables (RoPE cos/sin, row -> sample map, attention
+  // segments and work lists) and the attention plan.  A few geometries are
+  // kept on the device at once, each with its own pinned staging buffer, so
+  // a caller that alternates between geometries (a guided pair and a single
+  // sample, for instance) re-uploads nothing and the host never waits; a
+  // slot is only rebuilt for a geometry not seen among the last kGeoSlots.
+  static constexpr int kGeoSlots = 4;
+  struct GeoSlot {
+    std::vector<int32_t> key;  // empty: never filled
+    float *cos_t = nullptr, *sin_t = nullptr;
+    int32_t* row_sample = nullptr;
+    zimg::AttnSeg* segs = nullptr;
+    zimg::AttnItem* items = nullptr;
+    void* staging = nullptr;
+    hipEvent_t done = nullptr;  // the last upload from ``staging`` has completed
+    uint64_t last_use = 0;
+    int n_items_stage[3] = {0, 0, 0};
+    int attn_full[3] = {0, 0, 0};
+    int attn_split[3] = {1, 1, 1};
+  } geo[kGeoSlots];
+  uint64_t geo_clock = 0;
+  size_t staging_bytes = 0;
+  int64_t max_items = 0;
+  // views of the slot of the current geometry
   float *cos_t = nullptr, *sin_t = nullptr;
   int32_t* row_sample = nullptr;
   zimg::AttnSeg* segs = nullptr;    // [3][max_batch]
   zimg::AttnItem* items = nullptr;  // [3][max_items]
-  int64_t max_items = 0;
-
-  // host staging for tables (pinned) and the cached geometry key
-  void* staging = nullptr;
-  size_t staging_bytes = 0;
-  hipEvent_t staging_done = nullptr;
   std::vector<int32_t> table_key;
   int n_items_stage[3] = {0, 0, 0};
   int attn_full[3] = {0, 0, 0};   // (item, head) pairs of a stage computed whole
@@ -425,8 +444,8 @@ struct zimg_dit {
       return set_err(e == hipErrorOutOfMemory ? ZIMG_ENOMEM : ZIMG_EHIP, "hipMalloc(%zu) failed: %s", bytes,
                      hipGetErrorString(e));
     allocations.push_back(q);
-    e = hipMemset(q, 0, bytes ? bytes : 16);
-    if (e != hipSuccess) return set_err(ZIMG_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
+    e = hipMemsetAsync(q, 0, bytes ? bytes : 16, setup);
+    if (e != hipSuccess) return set_err(ZIMG_EHIP, "hipMemsetAsync failed: %s", hipGetErrorString(e));
     *p = (T*)q;
     return ZIMG_OK;
   }
@@ -443,8 +462,11 @@ struct zimg_dit {
   ~zimg_dit() {
     for (hipEvent_t e : prof.ev) (void)hipEventDestroy(e);
     for (void* p : allocations) (void)hipFree(p);
-    if (staging) (void)hipHostFree(staging);
-    if (staging_done) (void)hipEventDestroy(staging_done);
+    for (GeoSlot& g : geo) {
+      if (g.done) (void)hipEventSynchronize(g.done);
+      if (g.staging) (void)hipHostFree(g.staging);
+      if (g.done) (void)hipEventDestroy(g.done);
+    }
   }
 
   int allocate();
@@ -471,7 +493,8 @@ int zimg_dit::allocate() {
   const int64_t nb = (int64_t)blocks.size();
   ALLOC(normw, nb * 4 * D);
   ALLOC(mod_idx_d, nb);
-  HIP_TRY(hipMemcpy(mod_idx_d, mod_index.data(), nb * sizeof(int32_t), hipMemcpyHostToDevice));
+  HIP_TRY(hipMemcpyAsync(mod_idx_d, mod_index.data(), nb * sizeof(int32_t), hipMemcpyHostToDevice, setup));
+  HIP_TRY(hipStreamSynchronize(setup));  // mod_index is host memory
   fold_stride = (4 * nb + 1) * D;
   ALLOC(fold, (int64_t)c.max_batch * fold_stride);
   ALLOC(t1w, (int64_t)c.t_mid * c.adaln_dim);
@@ -582,12 +605,14 @@ int zimg_dit::allocate() {
   ALLOC(hmid, (int64_t)c.max_batch * c.t_mid);
   ALLOC(cvec, (int64_t)c.max_batch * c.adaln_dim);
   ALLOC(mod, (int64_t)c.max_batch * mod_stride);
-  ALLOC(cos_t, S_max * 64);
-  ALLOC(sin_t, S_max * 64);
-  ALLOC(row_sample, S_max);
   max_items = S_max / 16 + 2 * (int64_t)c.max_batch + 8;  // q-tiles of 128 over ranges of >= 16 rows
-  ALLOC(segs, 3 * (int64_t)c.max_batch);
-  ALLOC(items, 3 * max_items);
+  for (GeoSlot& gs : geo) {
+    ALLOC(gs.cos_t, S_max * 64);
+    ALLOC(gs.sin_t, S_max * 64);
+    ALLOC(gs.row_sample, S_max);
+    ALLOC(gs.segs, 3 * (int64_t)c.max_batch);
+    ALLOC(gs.items, 3 * max_items);
+  }
   int n_cu = 0;
   HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, device));
   split.n_cu = n_cu;
@@ -597,10 +622,14 @@ int zimg_dit::allocate() {
 #undef ALLOC
   staging_bytes = (size_t)S_max * 64 * 4 * 2 + (size_t)S_max * 4 + 3 * c.max_batch * sizeof(zimg::AttnSeg) +
                   3 * max_items * sizeof(zimg::AttnItem);
-  hipError_t e = hipHostMalloc(&staging, staging_bytes, hipHostMallocDefault);
-  if (e != hipSuccess) return set_err(ZIMG_ENOMEM, "hipHostMalloc(%zu) failed: %s", staging_bytes, hipGetErrorString(e));
-  HIP_TRY(hipEventCreateWithFlags(&staging_done, hipEventDisableTiming));
-  HIP_TRY(hipEventRecord(staging_done, nullptr));
+  for (GeoSlot& gs : geo) {
+    hipError_t e = hipHostMalloc(&gs.staging, staging_bytes, hipHostMallocDefault);
+    if (e != hipSuccess)
+      return set_err(ZIMG_ENOMEM, "hipHostMalloc(%zu) failed: %s", staging_bytes, hipGetErrorString(e));
+    HIP_TRY(hipEventCreateWithFlags(&gs.done, hipEventDisableTiming));
+    HIP_TRY(hipEventRecord(gs.done, setup));
+  }
+  HIP_TRY(hipStreamSynchronize(setup));  // the workspace clears have run
   return ZIMG_OK;
 }
 
@@ -626,7 +655,8 @@ int zimg_dit::set_weight(const zimg_tensor* w) {
     if (w->dtype == ZIMG_F32) std::memcpy(v.data(), w->data, n * 4);
     else
       for (int64_t i = 0; i < n; ++i) v[i] = bf16_to_f32(((const uint16_t*)w->data)[i]);
-    HIP_TRY(hipMemcpy(sl.dst, v.data(), n * 4, hipMemcpyHostToDevice));
+    HIP_TRY(hipMemcpyAsync(sl.dst, v.data(), n * 4, hipMemcpyHostToDevice, setup));
+    HIP_TRY(hipStreamSynchronize(setup));  // v is released on return
   } else {
     std::vector<uint16_t> tmp;
     const uint16_t* src = (const uint16_t*)w->data;
@@ -637,14 +667,15 @@ int zimg_dit::set_weight(const zimg_tensor* w) {
       src = tmp.data();
     }
     if (sl.kind == 0) {
-      HIP_TRY(hipMemcpy(sl.dst, src, n * 2, hipMemcpyHostToDevice));
+      HIP_TRY(hipMemcpyAsync(sl.dst, src, n * 2, hipMemcpyHostToDevice, setup));
     } else {
       // interleave 32-row groups: w1 rows go to 64g + r, w3 rows to 64g + 32 + r
       const int64_t cols = sl.cols;
       const int64_t half = sl.kind == 3 ? 32 : 0;
-      HIP_TRY(hipMemcpy2D((bf16_t*)sl.dst + half * cols, 64 * cols * 2, src, 32 * cols * 2, 32 * cols * 2,
-                          sl.rows / 32, hipMemcpyHostToDevice));
+      HIP_TRY(hipMemcpy2DAsync((bf16_t*)sl.dst + half * cols, 64 * cols * 2, src, 32 * cols * 2, 32 * cols * 2,
+                               sl.rows / 32, hipMemcpyHostToDevice, setup));
     }
+    HIP_TRY(hipStreamSynchronize(setup));  // the caller's array (or tmp) may go away on return
   }
   sl.set = true;
   return ZIMG_OK;
@@ -663,14 +694,14 @@ int zimg_dit::finalize() {
     // quantize every block projection per output row, then drop the bf16 copies
     const int D = cfg.hidden, F = cfg.ffn;
     for (BlockW& w : bw) {
-      HIP_TRY(zimg::launch_quant_rows(w.wqkv, 1, D, w.qqkv, D, w.sqkv, 3 * D, D, 0, 1.0f, nullptr));
-      HIP_TRY(zimg::launch_quant_rows(w.wo, 1, D, w.qo, D, w.so, D, D, 0, 1.0f, nullptr));
-      HIP_TRY(zimg::launch_quant_rows(w.w13, 1, D, w.q13, D, w.s13, 2 * F, D, 0, 1.0f, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.wqkv, 1, D, w.qqkv, D, w.sqkv, 3 * D, D, 0, 1.0f, setup));
+      HIP_TRY(zimg::launch_quant_rows(w.wo, 1, D, w.qo, D, w.so, D, D, 0, 1.0f, setup));
+      HIP_TRY(zimg::launch_quant_rows(w.w13, 1, D, w.q13, D, w.s13, 2 * F, D, 0, 1.0f, setup));
       // w2's input is rotated by 128-point Walsh-Hadamard blocks at run time;
       // its weight rows get the same transform, and their scales the 1/128
-      HIP_TRY(zimg::launch_quant_rows(w.w2, 1, F, w.q2, F, w.s2, D, F, 1, 1.0f / 128.0f, nullptr));
+      HIP_TRY(zimg::launch_quant_rows(w.w2, 1, F, w.q2, F, w.s2, D, F, 1, 1.0f / 128.0f, setup));
     }
-    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipStreamSynchronize(setup));
     for (BlockW& w : bw) {
       for (bf16_t** m : {&w.wqkv, &w.wo, &w.w13, &w.w2}) {
         dfree(*m);
@@ -693,9 +724,23 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
     key.push_back(L.Wl[b]);
     key.push_back(L.lens[b]);
   }
-  if (key != table_key) {
-    HIP_TRY(hipEventSynchronize(staging_done));  // previous upload has left the staging buffer
-    char* st = (char*)staging;
+  int slot = -1;
+  for (int i = 0; i < kGeoSlots; ++i)
+    if (geo[i].key == key) slot = i;
+  if (slot < 0) {
+    // a new geometry: rebuild the least recently used slot
+    slot = 0;
+    for (int i = 1; i < kGeoSlots; ++i)
+      if (geo[i].last_use < geo[slot].last_use) slot = i;
+    GeoSlot& G = geo[slot];
+    G.key.clear();
+    // its staging buffer was last read by an upload at least one geometry
+    // change ago; that upload has normally long completed
+    HIP_TRY(hipEventSynchronize(G.done));
+    int* n_items_stage = G.n_items_stage;
+    int* attn_full = G.attn_full;
+    int* attn_split = G.attn_split;
+    char* st = (char*)G.staging;
     float* cs = (float*)st;
     float* sn = cs + L.S * 64;
     int32_t* rs = (int32_t*)(sn + L.S * 64);
@@ -761,12 +806,27 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
         }
       }
     }
-    HIP_TRY(hipMemcpyAsync(cos_t, cs, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemcpyAsync(sin_t, sn, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemcpyAsync(row_sample, rs, (size_t)L.S * 4, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemcpyAsync(segs, sg, 3 * c.max_batch * sizeof(zimg::AttnSeg), hipMemcpyHostToDevice, s));
-    HIP_TRY(hipMemcpyAsync(items, itm, 3 * max_items * sizeof(zimg::AttnItem), hipMemcpyHostToDevice, s));
-    HIP_TRY(hipEventRecord(staging_done, s));
+    HIP_TRY(hipMemcpyAsync(G.cos_t, cs, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(G.sin_t, sn, (size_t)L.S * 64 * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(G.row_sample, rs, (size_t)L.S * 4, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(G.segs, sg, 3 * c.max_batch * sizeof(zimg::AttnSeg), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipMemcpyAsync(G.items, itm, 3 * max_items * sizeof(zimg::AttnItem), hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(G.done, s));
+    G.key = key;
+  }
+  {
+    GeoSlot& G = geo[slot];
+    G.last_use = ++geo_clock;
+    cos_t = G.cos_t;
+    sin_t = G.sin_t;
+    row_sample = G.row_sample;
+    segs = G.segs;
+    items = G.items;
+    for (int i = 0; i < 3; ++i) {
+      n_items_stage[i] = G.n_items_stage[i];
+      attn_full[i] = G.attn_full[i];
+      attn_split[i] = G.attn_split[i];
+    }
     table_key = key;
   }
 
@@ -1162,7 +1222,7 @@ int zimg_dit_manifest_entry(const zimg_dit_config* cfg, int32_t index, const cha
   return ZIMG_OK;
 }
 
-int zimg_dit_alloc(const zimg_dit_config* cfg, zimg_dit** out) {
+int zimg_dit_alloc(const zimg_dit_config* cfg, void* stream, zimg_dit** out) {
   g_last_error.clear();
   if (!out) return set_err(ZIMG_EINVAL, "out is NULL");
   *out = nullptr;
@@ -1174,6 +1234,7 @@ int zimg_dit_alloc(const zimg_dit_config* cfg, zimg_dit** out) {
     return set_err(ZIMG_EHIP, "no HIP device available: %s", e != hipSuccess ? hipGetErrorString(e) : "0 devices");
   std::unique_ptr<zimg_dit> h(new zimg_dit());
   h->cfg = *cfg;
+  h->setup = (hipStream_t)stream;
   HIP_TRY(hipGetDevice(&h->device));
   rc = h->allocate();
   if (rc) return rc;
@@ -1194,12 +1255,13 @@ int zimg_dit_finalize(zimg_dit* h) {
   return rc ? h->fail(rc) : ZIMG_OK;
 }
 
-int zimg_dit_create(const zimg_dit_config* cfg, const zimg_tensor* weights, int32_t n_weights, zimg_dit** out) {
+int zimg_dit_create(const zimg_dit_config* cfg, const zimg_tensor* weights, int32_t n_weights, void* stream,
+                    zimg_dit** out) {
   if (!out) return set_err(ZIMG_EINVAL, "out is NULL");
   *out = nullptr;
   if (n_weights < 0 || (n_weights > 0 && !weights)) return set_err(ZIMG_EINVAL, "bad weights array");
   zimg_dit* h = nullptr;
-  int rc = zimg_dit_alloc(cfg, &h);
+  int rc = zimg_dit_alloc(cfg, stream, &h);
   if (rc) return rc;
   for (int32_t i = 0; i < n_weights && !rc; ++i) rc = zimg_dit_set_weight(h, &weights[i]);
   if (!rc) rc = zimg_dit_finalize(h);
@@ -1446,6 +1508,35 @@ int zimg_dit_attention_plan(zimg_dit* h, int32_t stage, int32_t out[3]) {
   out[2] = h->attn_split[stage];
   return ZIMG_OK;
 }
+
+// The flow-match schedule, in float64 and in the order of operations of the
+// definition: base sigmas as an evenly spaced ramp from 1 down to 1/N
+// (sigma_i = 1 + i * ((1/N - 1) / (N - 1)), the last one exactly 1/N), the
+// shift s * sigma / (1 + (s - 1) * sigma), a final 0, and the model times
+// (1000 - 1000 sigma') / 1000.  Contraction into fused multiply-adds is off,
+// so every product and sum is rounded on its own.
+#pragma clang fp contract(off)
+int zimg_flowmatch_schedule(int32_t n_steps, double shift, double* sigmas, double* t) {
+  if (n_steps < 1 || n_steps > (1 << 20)) return set_err(ZIMG_EINVAL, "n_steps %d outside 1..2^20", n_steps);
+  if (!std::isfinite(shift) || shift <= 0.0) return set_err(ZIMG_EINVAL, "shift must be finite and positive");
+  if (!sigmas || !t) return set_err(ZIMG_EINVAL, "output array is NULL");
+  const double start = 1.0, stop = 1.0 / n_steps;
+  const double step = n_steps > 1 ? (stop - start) / (double)(n_steps - 1) : 0.0;
+  for (int32_t i = 0; i < n_steps; ++i) {
+    double base = (double)i * step;
+    base = base + start;
+    if (i == n_steps - 1) base = stop;
+    const double num = shift * base;
+    const double den = 1.0 + (shift - 1.0) * base;
+    const double sp = num / den;
+    sigmas[i] = sp;
+    const double thousand_sp = 1000.0 * sp;
+    t[i] = (1000.0 - thousand_sp) / 1000.0;
+  }
+  sigmas[n_steps] = 0.0;
+  return ZIMG_OK;
+}
+#pragma clang fp contract(on)
 
 int zimg_euler_step(float* x, const float* model_out, float dt, int64_t n, void* stream) {
   g_last_error.clear();

@@ -6,7 +6,8 @@ the zimage FastVideo port", Pinned official pipeline context): base sigmas
 linspace(1, 1/N, N), shifted sigma' = s sigma / (1 + (s - 1) sigma), a final
 sigma' = 0 appended (no model call there); model time t = (1000 - 1000
 sigma')/1000; each step x += (sigma'_{k+1} - sigma'_k) * (-model_out).  The
-schedule is computed on the host in float64; the update runs on the GPU.
+schedule comes from the library (zimg_flowmatch_schedule, host float64); the
+update runs on the GPU.
 """
 
 import numpy as np
@@ -16,11 +17,7 @@ from . import binding
 
 def schedule(n_steps, shift):
     """(shifted sigmas [N+1] ending at 0, model times [N]) in float64."""
-    base = np.linspace(1.0, 1.0 / n_steps, n_steps, dtype=np.float64)
-    shifted = shift * base / (1.0 + (shift - 1.0) * base)
-    sig = np.append(shifted, 0.0)
-    t = (1000.0 - 1000.0 * shifted) / 1000.0
-    return sig, t
+    return binding.flowmatch_schedule(n_steps, shift)
 
 
 def euler_loop(dit, latent, caption_feats, caption_lens, n_steps=8, shift=3.0, out=None, on_step=None,

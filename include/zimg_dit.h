@@ -135,11 +135,16 @@ int zimg_dit_manifest_entry(const zimg_dit_config* cfg, int32_t index,
  * unknown, duplicate or mis-shaped tensor).  The streaming variant
  * zimg_dit_alloc() + zimg_dit_set_weight() (one tensor at a time) +
  * zimg_dit_finalize() applies the same strict check at finalize.
+ * ``stream`` (a hipStream_t, NULL = the default stream; owned by the caller,
+ * who keeps it alive while the handle exists) carries the set-up work:
+ * workspace clears, weight uploads and repacking.  Each call returns once
+ * its work on that stream is done, so the caller may free its host weight
+ * arrays as soon as the call returns.
  * On failure *out is NULL and everything allocated is released.
  */
 int zimg_dit_create(const zimg_dit_config* cfg, const zimg_tensor* weights,
-                    int32_t n_weights, zimg_dit** out);
-int zimg_dit_alloc(const zimg_dit_config* cfg, zimg_dit** out);
+                    int32_t n_weights, void* stream, zimg_dit** out);
+int zimg_dit_alloc(const zimg_dit_config* cfg, void* stream, zimg_dit** out);
 int zimg_dit_set_weight(zimg_dit* h, const zimg_tensor* w);
 int zimg_dit_finalize(zimg_dit* h);
 

@@ -103,6 +103,23 @@ int zimg_quantize_rows(const void* x, int32_t x_dtype, int64_t ldx, int8_t* q, i
                        int32_t rows, int32_t K, int32_t rotate_block, void* stream);
 
 /*
+ * The FlowMatch Euler schedule of the sampler, on the host in float64
+ * ("Z-Image-Turbo MNN (int8, fp16-safe)", Scheduler: sigmas evenly spaced
+ * from 1 to 1/N, shifted by sigma' = s sigma / (1 + (s - 1) sigma), model
+ * time t = (1000 - 1000 sigma')/1000; "Local component coverage and quality
+ * handoff for the zimage FastVideo port", Pinned official pipeline context:
+ * N + 1 points ending at sigma' = 0, where no model call is made).
+ *   sigmas  HOST double [n_steps + 1]: sigma'_0 .. sigma'_{N-1}, then 0
+ *   t       HOST double [n_steps]: the model time of each step (1 = clean)
+ * Step k's Euler increment is sigmas[k + 1] - sigmas[k].  Each value is
+ * computed with separately rounded operations in the order written above
+ * (base sigma_i = i * ((1/N - 1)/(N - 1)) + 1, the last exactly 1/N), so the
+ * results are reproducible bit for bit.  ZIMG_EINVAL for n_steps outside
+ * 1..2^20, a shift that is not finite and positive, or NULL arrays.
+ */
+int zimg_flowmatch_schedule(int32_t n_steps, double shift, double* sigmas, double* t);
+
+/*
  * Euler update of the FlowMatch sampler: x[i] += dt * (-model_out[i]) for
  * i < n ("Z-Image-Turbo MNN (int8, fp16-safe)", Scheduler: the model output
  * is negated before the Euler step; dt = sigma'_{k+1} - sigma'_k).

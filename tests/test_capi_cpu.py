@@ -96,7 +96,7 @@ def test_alloc_without_gpu_fails_with_hip_error():
     b = _b()
     cfg = helpers.engine_config(synthetic.WORKLOADS["tiny_block"]["model"])
     h = ctypes.c_void_p()
-    rc = b.lib().zimg_dit_alloc(ctypes.byref(cfg), ctypes.byref(h))
+    rc = b.lib().zimg_dit_alloc(ctypes.byref(cfg), None, ctypes.byref(h))
     assert rc == b.ZIMG_EHIP and not h.value
     assert "HIP device" in b.lib().zimg_last_error().decode()
 
@@ -146,12 +146,37 @@ def test_row_layout_varsize():
 
 
 def test_sampler_schedule_equals_oracle():
+    """zimg_flowmatch_schedule (through sampler.schedule) equals the oracle's
+    float64 schedule bit for bit, for step counts 1..60 and several shifts."""
     from diffusion_transformer_image_amd import sampler
-    for n, s in [(8, 3.0), (28, 6.0), (1, 3.0)]:
-        es, et = sampler.schedule(n, s)
-        os_, ot = osm.schedule(n, s)
-        np.testing.assert_array_equal(es, os_)
-        np.testing.assert_array_equal(et, ot)
+    for n in list(range(1, 61)) + [1000]:
+        for s in (1.0, 3.0, 6.0, 2.5):
+            es, et = sampler.schedule(n, s)
+            os_, ot = osm.schedule(n, s)
+            assert es.view(np.uint64).tolist() == os_.view(np.uint64).tolist(), (n, s)
+            assert et.view(np.uint64).tolist() == ot.view(np.uint64).tolist(), (n, s)
+
+
+def test_flowmatch_schedule_against_exact_fractions(golden):
+    """The 8-step shift-3 schedule against the hand-derived fractions: each
+    shifted sigma is one correctly rounded division of exactly representable
+    values, so it is the nearest double of the fraction, bit for bit; t and
+    the increments are within one rounding of theirs."""
+    from fractions import Fraction
+    g = golden["sampler_schedule"]
+    sig, t = _b().flowmatch_schedule(g["n_steps"], g["shift"])
+    assert [float(Fraction(v)) for v in g["sigma_shifted"]] == sig.tolist()
+    for got, want in zip(t, g["t"]):
+        assert abs(got - float(Fraction(want))) <= 2e-16
+    for k, want in enumerate(g["dt"]):
+        assert abs((sig[k + 1] - sig[k]) - float(Fraction(want))) <= 4e-16
+
+
+@pytest.mark.parametrize("n,shift", [(0, 3.0), (-2, 3.0), (8, 0.0), (8, float("nan")), (8, -1.0)])
+def test_flowmatch_schedule_rejects_bad_arguments(n, shift):
+    with pytest.raises(_b().ZimgError) as ei:
+        _b().flowmatch_schedule(n, shift)
+    assert ei.value.code == _b().ZIMG_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch):
