@@ -94,6 +94,5 @@ def test_split_attention_blocks_vs_oracle(engine, case):
             want = om.block(ocfg, Wo, prefix, xin, cos, sin, mod)
             got = got_all[rows]
             r, cs = helpers.assert_parity(got, want, f"case {case} sample {b} {prefix}")
-            rb = helpers.rel_l2(got - xin, want - xin)
-            assert rb <= 3e-2, f"case {case} sample {b} {prefix}: branch rel-L2 {rb:.3e}"
-            print(f"  sample {b}: rel-L2 {r:.2e} cos {cs:.7f} branch {rb:.2e}")
+            rb, rw = helpers.assert_branch(got, xin, want, xin, f"case {case} sample {b} {prefix}")
+            print(f"  sample {b}: rel-L2 {r:.2e} cos {cs:.7f} branch {rb:.2e} worst row {rw:.2e}")

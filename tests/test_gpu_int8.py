@@ -46,6 +46,7 @@ INT8_COS_GATE = 0.9996
 I8_REL_TOL = 3e-2
 I8_COS_TOL = 0.9995
 I8_BRANCH_TOL = 5e-2
+I8_ROW_BRANCH_TOL = 1e-1  # the worst single row: twice the aggregate bar
 
 
 def _torch():
@@ -261,9 +262,10 @@ def _forward_vs_oracle(model, latent_shape, lens, t, seed=0, batch_invariant=0):
                     gin, oin = g_prev, o_prev
                 g_prev, o_prev = got, want
             r, _ = helpers.assert_parity(got, want, f"int8 sample {b} {p}", I8_REL_TOL, I8_COS_TOL)
-            rb = helpers.rel_l2(got - gin, want - oin)
-            assert rb <= I8_BRANCH_TOL, f"int8 sample {b} {p}: branch rel-L2 {rb:.3e}"
+            rb, rw = helpers.assert_branch(got, gin, want, oin, f"int8 sample {b} {p}", I8_BRANCH_TOL,
+                                           I8_ROW_BRANCH_TOL)
             worst["rel"], worst["branch"] = max(worst["rel"], r), max(worst["branch"], rb)
+            worst["row_branch"] = max(worst.get("row_branch", 0.0), rw)
         _, cq = helpers.assert_parity(out[b], ref_q, f"int8 sample {b} final output vs the int8 oracle",
                                       I8_REL_TOL, I8_COS_TOL)
         cf = helpers.cosine(out[b], ref_f)

@@ -62,7 +62,7 @@ def test_varsize_batch_vs_oracle():
     ocfg = helpers.oracle_config(SMALL)
     Wo = helpers.oracle_weights(SMALL, seed=7).materialize(workers=4)
     prefixes = [p for p, _ in block_prefixes(ocfg)]
-    worst = 0.0
+    worst, worst_row = 0.0, 0.0
     for b in range(3):
         c = {}
         ref = om.forward_sample(ocfg, Wo, lats[b], caps[b], float(np.float32(TIMES[b])), capture=c)
@@ -70,19 +70,30 @@ def test_varsize_batch_vs_oracle():
         rc = cap_off[b] + np.arange(LENS[b])
         helpers.assert_parity(capt[0][ri], c["x_embed"], f"sample {b} x_embed")
         helpers.assert_parity(capt[0][rc], c["cap_embed"], f"sample {b} cap_embed")
+        # block inputs of each side: the branch check subtracts each side's own input
+        g_img, g_cap, o_img, o_cap = capt[0][ri], capt[0][rc], c["x_embed"], c["cap_embed"]
+        g_prev = o_prev = None
         for i, p in enumerate(prefixes):
             slot = capt[i + 1]
             if p.startswith("noise_refiner"):
-                got = slot[ri]
+                got, gin, oin = slot[ri], g_img, o_img
+                g_img, o_img = got, c[p]
             elif p.startswith("context_refiner"):
-                got = slot[rc]
+                got, gin, oin = slot[rc], g_cap, o_cap
+                g_cap, o_cap = got, c[p]
             else:
                 got = np.concatenate([slot[ri], slot[rc]])
+                if o_prev is None:
+                    gin, oin = np.concatenate([g_img, g_cap]), np.concatenate([o_img, o_cap])
+                else:
+                    gin, oin = g_prev, o_prev
+                g_prev, o_prev = got, c[p]
             r, _ = helpers.assert_parity(got, c[p], f"sample {b} {p}")
-            worst = max(worst, r)
+            _, rw = helpers.assert_branch(got, gin, c[p], oin, f"sample {b} {p}")
+            worst, worst_row = max(worst, r), max(worst_row, rw)
         r, _ = helpers.assert_parity(outs[b].cpu().numpy(), ref, f"sample {b} final output")
         worst = max(worst, r)
-    print(f"worst rel-L2 {worst:.2e}")
+    print(f"worst rel-L2 {worst:.2e}, worst row branch rel-L2 {worst_row:.2e}")
 
 
 def test_varsize_sample_alone_equals_in_batch():
