@@ -29,9 +29,9 @@ WORKLOADS = {
         model=dict(FULL_MODEL),
         latent=(1, 16, 256, 256), caption_lens=(512,), t=(0.5,), seed=0),
     # 8-step Euler loop at 1536x640, batch 2, captions of 77 and 300 tokens,
-    # w2 outliers scaled by 2**17 (|w2 output| peaks near 1e6)
+    # w2 outliers scaled by 2**16 (|w2 output| peaks in (5e5, 1e6])
     "euler_1536x640": dict(
         model=dict(FULL_MODEL),
         latent=(2, 16, 192, 80), caption_lens=(77, 300), t=None, seed=0,
-        steps=8, shift=3.0, outlier_log2=17),
+        steps=8, shift=3.0, outlier_log2=16),
 }

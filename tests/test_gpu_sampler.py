@@ -1,10 +1,11 @@
 """The 8-step FlowMatch Euler workload (shift 3, batch 2, captions of 77 and
-300 tokens, FFN w2 outputs with outliers near 1e6).
+300 tokens, FFN w2 outputs with outliers up to ~1e6).
 
-At reduced width the whole loop runs against the oracle's loop (the float64
-oracle cannot run 8 x 2 full-width forwards in a test); at full width and the
-workload's 1536x640 geometry the loop is checked for finiteness, bitwise
-reproducibility, and batch independence (each sample run alone matches its
+At reduced width the whole loop runs against the oracle's loop; at full
+width and the workload's 1536x640 geometry the loop runs against the float64
+oracle's outputs stored by tests/golden/make_fullsize_outputs.py (the oracle
+needs about 20 minutes of CPU per full-width step of the pair), and is
+checked for finiteness, bitwise reproducibility, and batch independence (each sample run alone matches its
 row of the batch to the parity bar; not bitwise: the batch size changes the
 GEMM tile counts and attention work items, and so which of them are split
 along K or keys, i.e. the fp32 summation order, and after 8 x 34 blocks
@@ -83,6 +84,50 @@ def test_euler_loop_reduced_width_vs_oracle(quant):
         assert cf >= INT8_COS_GATE, f"final latent cosine {cf:.6f} against the float oracle's loop"
         msg += f"; vs the float loop cos {cf:.7f}"
     print(msg)
+    dit.close()
+
+
+def _golden():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "euler_1536x640_oracle_outputs.npz")
+    if not os.path.exists(path):
+        return None, None
+    z = np.load(path)
+    return {k: z[k] for k in z.files if k != "meta"}, json.loads(str(z["meta"]))
+
+
+def test_euler_loop_full_size_vs_stored_oracle():
+    """The full-width loop at 1536x640, batch 2, captions 77 / 300, w2
+    outliers: the step-0 model output of the batch against the stored
+    float64 oracle output (every sample at the parity bar), and, where the
+    oracle's whole 8-step loop is stored, every step's model output and the
+    final latent."""
+    torch = _torch()
+    from diffusion_transformer_image_amd import euler_loop
+    wl = synthetic.WORKLOADS["euler_1536x640"]
+    gold, meta = _golden()
+    if gold is None:
+        pytest.skip("tests/golden/euler_1536x640_oracle_outputs.npz not written")
+    assert meta["outlier_log2"] == wl["outlier_log2"] and meta["caption_lens"] == list(wl["caption_lens"])
+    lens, shape = wl["caption_lens"], wl["latent"]
+    dit = _engine(wl["model"], 2, (shape[2] // 2) * (shape[3] // 2), max(lens), wl["outlier_log2"])
+    lat = synthetic.latent(shape, seed=wl["seed"])
+    caps = synthetic.captions(lens, seed=wl["seed"])
+    x = torch.from_numpy(lat).cuda()
+    outs = []
+    euler_loop(dit, x, torch.from_numpy(np.concatenate(caps)).cuda(), lens, n_steps=wl["steps"], shift=wl["shift"],
+               on_step=lambda k, xx, o: outs.append(o.cpu().numpy()))
+    torch.cuda.synchronize()
+    for b in range(2):
+        r, c = helpers.assert_parity(outs[0][b], gold["out0"][b].astype(np.float64), f"step 0 sample {b}")
+        print(f"step 0 sample {b}: rel-L2 {r:.2e} cos {c:.7f}")
+    if "final" in gold:
+        for k in range(wl["steps"]):
+            r, c = helpers.assert_parity(outs[k], gold["outs"][k].astype(np.float64), f"step {k} model output")
+            print(f"step {k}: rel-L2 {r:.2e} cos {c:.7f}")
+        r, c = helpers.assert_parity(x.cpu().numpy(), gold["final"].astype(np.float64), "final latent")
+        print(f"final latent after {wl['steps']} steps: rel-L2 {r:.2e} cos {c:.7f}")
     dit.close()
 
 

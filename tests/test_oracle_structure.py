@@ -72,3 +72,26 @@ def test_image_token_counts(golden):
         C, Hl, Wl = it["latent"][res]
         tok = om.patchify(np.zeros((C, Hl, Wl)), 2)
         assert tok.shape == (n, 64)
+
+
+def test_euler_workload_outlier_peak_in_range():
+    """Reading of the outlier injection ("Z-Image-Turbo MNN (int8,
+    fp16-safe)", Conversion details: w2 outputs with outliers up to about
+    1e6): the power-of-two scale of the 4 seeded w2 rows per block is the one
+    that puts the oracle's largest |w2 output| over the loop's first step
+    (every row of every block, both samples) in (5e5, 1e6].  Checked on the
+    stored oracle outputs of that step."""
+    import json
+    import os
+    import numpy as np
+    import pytest
+    import synthetic
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "euler_1536x640_oracle_outputs.npz")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle outputs of the Euler workload not written")
+    z = np.load(path)
+    meta = json.loads(str(z["meta"]))
+    assert meta["outlier_log2"] == synthetic.WORKLOADS["euler_1536x640"]["outlier_log2"]
+    peaks = z["ffn_peak"]
+    assert peaks.shape == (2, 34)
+    assert 5e5 < peaks.max() <= 1e6, peaks.max()
