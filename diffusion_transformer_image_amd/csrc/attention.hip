@@ -182,15 +182,19 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = -INFINITY, lp[4] = {0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lp[2] = {0.f, 0.f};
   const float sl2 = a.scale_log2;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Online softmax in the log2 domain (raw v_exp_f32: weights below 2^-126
   // flush to zero).  The reference max m only moves when a lane's max exceeds
   // it by the slack, so p <= 2^slack; O and l are rescaled only when some lane
   // of the wave moved its m (a wave-uniform branch; after the first tile of a
   // row this is rare), since the rescale is as much vector work as the
-  // exponentials themselves.
+  // exponentials themselves.  m is always an integer (the ceiling of the
+  // max), so a weight 2^(s - m) rounds to bf16 the same way whatever m is:
+  // a pair split into key chunks (each with its own m) weighs every key as
+  // the whole pair would, and the merge scales chunks by exact powers of two.
   auto stats = [&](f32x16* st) {
     float mx = -INFINITY;
 #pragma unroll
@@ -198,11 +202,11 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[tt][e]);
     mx = pair_max(mx) * sl2;
-    const float mnew = mx > m + RESCALE_SLACK ? mx : m;
+    const float mnew = mx > m + RESCALE_SLACK ? ceilf(mx) : m;
     if (__any(mnew != m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lp[i] *= alpha;
+      for (int i = 0; i < 2; ++i) lp[i] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -210,19 +214,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       m = mnew;
     }
   };
-  // the row sum of this lane's keys in four running parts (short dependency
-  // chains); the parts and the lane pair are summed once, at the end
   auto expsum = [&](f32x16* st) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[tt][e], sl2, -m));
-        st[tt][e] = p;
-        lp[e & 3] += p;
-      }
+      for (int e = 0; e < 16; ++e) st[tt][e] = __builtin_amdgcn_exp2f(fmaf(st[tt][e], sl2, -m));
   };
-  // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step)
+  // O^T += V^T P^T over 4 key-steps of 16 (P converted to bf16 per step).
+  // The row sum l adds up the same bf16 weights the product uses, two per
+  // dot instruction, in two running parts (the parts and the lane pair are
+  // summed once, at the end), so the normalised weights sum to one.
   auto pv = [&](const bf16_t* vb, const f32x16* st) {
     auto vread = [&](int i) {  // i = 4 s + dt
       return *reinterpret_cast<const bf16x8*>(vb + ((i & 3) * 32 + lrow) * KTILE + (((2 * (i >> 2) + lhalf) ^ swv) << 3));
@@ -237,6 +238,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       if ((i & 3) == 0) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) pf[u] = (__bf16)st[i >> 3][((i >> 2) & 1) * 8 + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          lp[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[2 * u], pf[2 * u + 1]}, ones, lp[u & 1], false);
       }
       o[i & 3] = mfma32(vf[i % (AHEAD + 1)], pf, o[i & 3]);
     }
@@ -249,13 +253,13 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     for (int g = 0; g < 16; ++g) {
       if (g + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU (exponentials)
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (exponentials)
     }
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first V operand reads
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
       if (g + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (V operand)
-      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (conversion, row sums)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
     }
   };
@@ -274,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     pin_order();
     // keeps the row-sum additions inside this half's interleave (otherwise
     // they are sunk past the next barrier, into the next half's serial part)
-    asm volatile("" : "+v"(lp[0]), "+v"(lp[1]), "+v"(lp[2]), "+v"(lp[3]));
+    asm volatile("" : "+v"(lp[0]), "+v"(lp[1]));
   };
 
   // The tile count is padded to an even number (>= 2) with an empty tile
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // no load may still be writing this workgroup's LDS when it ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const float l = pair_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
+  const float l = pair_sum(lp[0] + lp[1]);
   if (qi < it.nq && unit >= 0) {
     // partial state of this chunk: O unnormalised (relative to 2^m), m, l
     float* po = a.part + (int64_t)unit * (128 * HD) + qi * HD;
@@ -369,7 +373,8 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
 }
 
 // Merge the chunks of one split (item, head) pair: with M the largest chunk
-// reference max, weight w_c = 2^(m_c - M); O = sum_c w_c O_c / sum_c w_c l_c,
+// reference max, weight w_c = 2^(m_c - M) (exact: the m_c are integers);
+// O = sum_c w_c O_c / sum_c w_c l_c,
 // summed in chunk order.  One workgroup per (pair, slice of CQ queries), so
 // the merge spreads over many CUs; 16 lanes per query, 8 dims each, with all
 // chunks' loads in flight together.

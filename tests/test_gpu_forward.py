@@ -137,13 +137,12 @@ def test_forward_degenerate_geometries(latent, lens):
 
 
 # alone vs in batch with the default splits: the batch changes which GEMM
-# tiles are split along K (fp32 summation order) and which attention pairs
-# are split along keys; a split chunk rounds its probabilities to bf16
-# relative to its own running max, so those roundings differ from the
-# unsplit pair's, by about the bf16 step per weight.  With zero-mean values
-# that noise does not average out in the weighted sum, which puts the two
-# runs ~2e-3 apart after this 4-block model (measured 2.2e-3)
-SPLIT_ORDER_TOL = 5e-3
+# tiles are split along K and which attention pairs are split along keys
+# (here sample 0's joint pairs run in two key chunks alone and whole in the
+# batch), i.e. the fp32 summation order, and so some bf16 roundings of the
+# activations downstream.  Measured 1.1e-3 after this 4-block model (sample
+# 1: bitwise equal); the bar is three times that
+SPLIT_ORDER_TOL = 3e-3
 
 
 @pytest.mark.parametrize("batch_invariant", [0, 1])
