@@ -103,6 +103,8 @@ SIGNATURES = {
     "zimg_dit_profile": (_I32, [_P, _I32]),
     "zimg_dit_profile_read": (_I32, [_P, ctypes.POINTER(KernelStat), _I32, _I32P]),
     "zimg_dit_attention_plan": (_I32, [_P, _I32, _I32P]),
+    "zimg_attention_workspace_size": (_I32, [_I32, _I32, _I32P, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "zimg_attention": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -484,6 +486,48 @@ def cfg_euler_step(x, out_cond, out_uncond, guidance, dt, stream=None):
     _check(lib().zimg_cfg_euler_step(_ptr(x), _ptr(out_cond), _ptr(out_uncond), float(guidance), float(dt),
                                      x.numel(), _stream(stream)))
     return x
+
+
+def _attention_args(qkv, vT, out, H, segments):
+    import torch
+    _want(qkv, "qkv", (torch.bfloat16,), 2, contiguous=True)
+    _want(vT, "vT", (torch.bfloat16,), 2, contiguous=True)
+    _want(out, "out", (torch.bfloat16,), 2, contiguous=True)
+    D = int(H) * 128
+    seg = np.ascontiguousarray(segments, dtype=np.int32).reshape(-1, 4)
+    if qkv.shape[1] != 3 * D or vT.shape[0] != D or out.shape[1] != D:
+        raise ValueError(f"qkv must be [rows, {3 * D}], vT [{D}, S_pad] and out [rows, {D}]")
+    ends = np.maximum(seg[:, 0] + seg[:, 1], seg[:, 2] + seg[:, 3]) if len(seg) else np.zeros(0)
+    if len(seg) and (int(ends.max()) > qkv.shape[0] or int(ends.max()) > out.shape[0]):
+        raise ValueError("a segment reaches past the rows of qkv or out")
+    return seg, vT.shape[1]
+
+
+def attention_workspace_size(H, segments, S_pad):
+    seg = np.ascontiguousarray(segments, dtype=np.int32).reshape(-1, 4)
+    n = ctypes.c_size_t()
+    _check(lib().zimg_attention_workspace_size(int(H), len(seg), seg.ctypes.data_as(_I32P), int(S_pad),
+                                               ctypes.byref(n)))
+    return n.value
+
+
+def attention(qkv, vT, out, H, segments, workspace=None, stream=None):
+    """The block's attention on torch CUDA buffers in the engine's layout
+    (zimg_attention): qkv bf16 [rows, 3 H 128], vT bf16 [H 128, S_pad],
+    out bf16 [rows, H 128]; segments [B][4] = (start, rows, start, rows).
+    ``workspace``: a uint8 CUDA tensor (default: one of the size
+    zimg_attention_workspace_size gives, allocated here)."""
+    import torch
+    seg, S_pad = _attention_args(qkv, vT, out, H, segments)
+    if workspace is None:
+        n = attention_workspace_size(H, seg, S_pad)
+        workspace = torch.empty(n + 256, dtype=torch.uint8, device=qkv.device)
+        off = (-workspace.data_ptr()) % 256
+        workspace = workspace[off:off + n]
+    _want(workspace, "workspace", (torch.uint8,), 1, contiguous=True)
+    _check(lib().zimg_attention(_ptr(qkv), _ptr(vT), S_pad, _ptr(out), int(H), len(seg), seg.ctypes.data_as(_I32P),
+                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
 
 
 def flowmatch_schedule(n_steps, shift):

@@ -429,7 +429,24 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   *reinterpret_cast<u32x4*>(a.out + (int64_t)(it.q0 + q) * (a.H * HD) + h * HD + d) = u;
 }
 
+__global__ __launch_bounds__(256) void attention_plan_kernel(AttnPlanArgs p) {
+  const int b = blockIdx.x;
+  const AttnSeg sg = p.seg[b];
+  if (threadIdx.x == 0) p.segs[b] = sg;
+  const int t0 = (sg.n[0] + 127) / 128, t1 = (sg.n[1] + 127) / 128;
+  for (int k = threadIdx.x; k < t0 + t1; k += blockDim.x) {
+    const int r = k < t0 ? 0 : 1, q = k < t0 ? k : k - t0;
+    p.items[p.item_off[b] + k] = AttnItem{sg.r0[r] + q * 128, min(128, sg.n[r] - q * 128), b, 0};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_attention_plan(const AttnPlanArgs& p, hipStream_t s) {
+  if (p.B <= 0 || p.B > ATTN_OP_MAX_B) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attention_plan_kernel, dim3(p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int total = a.n_items * a.H;

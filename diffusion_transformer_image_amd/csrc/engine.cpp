@@ -1165,6 +1165,104 @@ int run_forward(zimg_dit* h, const float* const* latents, int32_t B, const int32
 
 }  // namespace
 
+// ------------------------------------------------------------------ attention op
+
+namespace {
+
+// Work list and split plan of the attention op for B samples with segments
+// seg [B][4] = (r0 of the first range, its rows, r0 of the second, its rows).
+struct AttnOpPlan {
+  int n_items = 0, n_full = 0, split = 1;
+  size_t header = 0;      // bytes of the work list at the start of the workspace
+  size_t part_bytes = 0;  // bytes of split partials the plan uses
+  zimg::AttnPlanArgs pa{};
+};
+
+int attention_op_plan(int32_t H, int32_t B, const int32_t* seg, int64_t S_pad, size_t ws_bytes, AttnOpPlan& P) {
+  if (H < 1 || H > 256) return set_err(ZIMG_EINVAL, "attention: H %d outside 1..256", H);
+  if (B < 1 || B > zimg::ATTN_OP_MAX_B) return set_err(ZIMG_EINVAL, "attention: B %d outside 1..%d", B, zimg::ATTN_OP_MAX_B);
+  if (!seg) return set_err(ZIMG_EINVAL, "attention: segments array is NULL");
+  if (S_pad < 64 || S_pad % 8 || S_pad > (1 << 24)) return set_err(ZIMG_EINVAL, "attention: S_pad %lld must be a multiple of 8 in 64..2^24", (long long)S_pad);
+  P.pa.B = B;
+  int n = 0;
+  for (int b = 0; b < B; ++b) {
+    zimg::AttnSeg& q = P.pa.seg[b];
+    for (int r = 0; r < 2; ++r) {
+      const int64_t r0 = seg[4 * b + 2 * r], len = seg[4 * b + 2 * r + 1];
+      if (len < 0 || r0 < 0 || r0 % 8) return set_err(ZIMG_EINVAL, "attention: sample %d range %d: start %lld must be a non-negative multiple of 8 and length %lld non-negative", b, r, (long long)r0, (long long)len);
+      if (r == 0 && len < 1) return set_err(ZIMG_EINVAL, "attention: sample %d: the first range is empty", b);
+      if (len > 0 && r0 + (len + 63) / 64 * 64 > S_pad)
+        return set_err(ZIMG_EINVAL, "attention: sample %d range %d: rows %lld..%lld (rounded up to 64 keys) exceed S_pad %lld", b, r, (long long)r0, (long long)(r0 + len), (long long)S_pad);
+      q.r0[r] = (int)r0;
+      q.n[r] = (int)len;
+    }
+    P.pa.item_off[b] = n;
+    n += (q.n[0] + 127) / 128 + (q.n[1] + 127) / 128;
+  }
+  P.pa.item_off[B] = n;
+  P.n_items = n;
+  P.header = (1024 + (size_t)16 * n + 255) / 256 * 256;
+  if ((int64_t)n * H > (1 << 30)) return set_err(ZIMG_EINVAL, "attention: too many work items");
+  if (ws_bytes < P.header)
+    return set_err(ZIMG_EINVAL, "attention: workspace of %zu bytes is smaller than the %zu-byte work list", ws_bytes, P.header);
+  int dev = 0, n_cu = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  // the engine's rule: two attention workgroups are resident per CU; a last
+  // round at most half full is split along keys (chunks of >= 2 key tiles)
+  const int total = n * H, Pslots = 2 * n_cu, r = total % Pslots;
+  P.n_full = total;
+  P.split = 1;
+  if (r > 0 && 2 * r <= Pslots) {
+    int tmin = 1 << 30;
+    for (int lid = total - r; lid < total; ++lid) {
+      const int item = lid % n;
+      int b = 0;
+      while (P.pa.item_off[b + 1] <= item) ++b;
+      const zimg::AttnSeg& q = P.pa.seg[b];
+      tmin = std::min(tmin, (q.n[0] + 63) / 64 + (q.n[1] + 63) / 64);
+    }
+    int sp = std::min(std::min(Pslots / r, tmin / 2), 16);
+    while (sp >= 2 && P.header + (size_t)r * sp * zimg::ATTN_PART_FLOATS * 4 > ws_bytes) --sp;
+    if (sp >= 2) {
+      P.n_full = total - r;
+      P.split = sp;
+      P.part_bytes = (size_t)r * sp * zimg::ATTN_PART_FLOATS * 4;
+    }
+  }
+  return ZIMG_OK;
+}
+
+int attention_op(const void* qkv, const void* vT, int64_t S_pad, void* out, int32_t H, int32_t B, const int32_t* seg,
+                 void* ws, size_t ws_bytes, hipStream_t s) {
+  if (!qkv || !vT || !out || !ws) return set_err(ZIMG_EINVAL, "attention: NULL buffer");
+  if (((uintptr_t)qkv & 15) || ((uintptr_t)vT & 15) || ((uintptr_t)out & 7) || ((uintptr_t)ws & 255))
+    return set_err(ZIMG_EINVAL, "attention: qkv and vT must be 16-byte, out 8-byte and the workspace 256-byte aligned");
+  AttnOpPlan P;
+  int rc = attention_op_plan(H, B, seg, S_pad, ws_bytes, P);
+  if (rc) return rc;
+  char* w = (char*)ws;
+  P.pa.segs = (zimg::AttnSeg*)w;
+  P.pa.items = (zimg::AttnItem*)(w + 1024);
+  HIP_TRY(zimg::launch_attention_plan(P.pa, s));
+  zimg::AttnArgs aa{(const bf16_t*)qkv,
+                    (const bf16_t*)vT,
+                    (bf16_t*)out,
+                    P.pa.items,
+                    P.pa.segs,
+                    P.n_items,
+                    H,
+                    (int)S_pad,
+                    (float)(1.4426950408889634 / std::sqrt(128.0)),
+                    P.n_full,
+                    P.split,
+                    (float*)(w + P.header)};
+  HIP_TRY(zimg::launch_attention(aa, s));
+  return ZIMG_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* zimg_last_error(void) { return g_last_error.c_str(); }
@@ -1507,6 +1605,22 @@ int zimg_dit_attention_plan(zimg_dit* h, int32_t stage, int32_t out[3]) {
   out[1] = h->attn_full[stage];
   out[2] = h->attn_split[stage];
   return ZIMG_OK;
+}
+
+
+int zimg_attention_workspace_size(int32_t H, int32_t B, const int32_t* seg, int64_t S_pad, size_t* bytes) {
+  if (!bytes) return set_err(ZIMG_EINVAL, "bytes is NULL");
+  AttnOpPlan P;
+  int rc = attention_op_plan(H, B, seg, S_pad, (size_t)-1, P);
+  if (rc) return rc;
+  *bytes = P.header + P.part_bytes;
+  return ZIMG_OK;
+}
+
+int zimg_attention(const void* qkv, const void* vT, int64_t S_pad, void* out, int32_t H, int32_t B,
+                   const int32_t* seg, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  return attention_op(qkv, vT, S_pad, out, H, B, seg, workspace, ws_bytes, (hipStream_t)stream);
 }
 
 // The flow-match schedule, in float64 and in the order of operations of the

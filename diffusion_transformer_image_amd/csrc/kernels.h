@@ -166,6 +166,19 @@ struct AttnArgs {
 constexpr int ATTN_PART_FLOATS = 128 * 128 + 2 * 128;
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// Work list of the attention op on caller buffers, written on the device:
+// segs[b] = seg[b], and sample b's q-tiles of 128 rows (its first range's,
+// then its second's) at items[item_off[b] ...].  One workgroup per sample.
+constexpr int ATTN_OP_MAX_B = 64;
+struct AttnPlanArgs {
+  int B;
+  AttnSeg seg[ATTN_OP_MAX_B];
+  int item_off[ATTN_OP_MAX_B + 1];
+  AttnSeg* segs;
+  AttnItem* items;
+};
+hipError_t launch_attention_plan(const AttnPlanArgs& p, hipStream_t s);
+
 // ---------------------------------------------------------------- small ops
 // latent fp32 [B, C, Hp*p, Wp*p] -> tokens bf16, row b*npad + i*Wp + j, width p*p*C
 hipError_t launch_patchify(const float* latent, bf16_t* out, int B, int C, int Hp, int Wp,

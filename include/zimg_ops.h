@@ -167,6 +167,37 @@ int zimg_dit_profile(zimg_dit* h, int32_t enable);
 int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
 /*
+ * The block's attention on caller buffers in the engine's layout: for each
+ * sample b, the queries and keys are the rows of its two ranges of the
+ * sequence buffer, o = softmax(q k^T / sqrt(128)) v per head, and no row
+ * attends to another sample's rows ("Z-Image" (AI Toolkit docs),
+ * Architecture: full bidirectional attention over one sample's shared
+ * text + image sequence, heads of 128; "Local component coverage and quality
+ * handoff for the zimage FastVideo port", Transformer: SDPA with a key mask
+ * per sample).  bf16 operands, fp32 online softmax.
+ *   qkv   DEVICE bf16 [rows, 3 H 128]: row r holds q (H x 128), k, then v
+ *         (the v part is not read), q and k already QK-normalised and rotated;
+ *         16-byte aligned
+ *   vT    DEVICE bf16 [H 128][S_pad]: v transposed (element [h 128 + d][r]),
+ *         16-byte aligned; S_pad a multiple of 8, 64..2^24
+ *   out   DEVICE bf16 [rows, H 128], 8-byte aligned; only the rows of the
+ *         segments are written
+ *   seg   HOST int32 [B][4]: (start, rows) of the first range, (start, rows)
+ *         of the second (rows may be 0); starts multiples of 8; each range,
+ *         its length rounded up to 64, must lie inside [0, S_pad)
+ *   workspace  DEVICE, 256-byte aligned, ws_bytes long: the work list and
+ *         the partial results of pairs split along keys (caller-owned; no
+ *         state survives a call).  zimg_attention_workspace_size() gives
+ *         the size that allows the plan the engine would use; a smaller
+ *         workspace (at least the work list) runs with fewer or no splits.
+ * B in 1..64, H in 1..256.  Asynchronous on ``stream``; ZIMG_EINVAL for bad
+ * arguments (nothing is enqueued).
+ */
+int zimg_attention_workspace_size(int32_t H, int32_t B, const int32_t* seg, int64_t S_pad, size_t* bytes);
+int zimg_attention(const void* qkv, const void* vT, int64_t S_pad, void* out, int32_t H, int32_t B,
+                   const int32_t* seg, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Attention work decomposition chosen for one stage (0: noise refiner, the
  * image rows; 1: context refiner, the caption rows; 2: joint blocks, all
  * rows) at the geometry of the most recent forward or run_blocks call on the
