@@ -105,6 +105,7 @@ SIGNATURES = {
     "zimg_dit_attention_plan": (_I32, [_P, _I32, _I32P]),
     "zimg_attention_workspace_size": (_I32, [_I32, _I32, _I32P, _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "zimg_attention": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32P, _P, ctypes.c_size_t, _P]),
+    "zimg_attention_noalloc": (_I32, [_P, _P, _I64, _P, _I32, _I32, _I32P, _P]),
 }
 
 _lib = None
@@ -527,6 +528,15 @@ def attention(qkv, vT, out, H, segments, workspace=None, stream=None):
     _want(workspace, "workspace", (torch.uint8,), 1, contiguous=True)
     _check(lib().zimg_attention(_ptr(qkv), _ptr(vT), S_pad, _ptr(out), int(H), len(seg), seg.ctypes.data_as(_I32P),
                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def attention_noalloc(qkv, vT, out, H, segments, stream=None):
+    """zimg_attention_noalloc: the attention op with the library's static
+    device scratch (no workspace, nothing allocated)."""
+    seg, S_pad = _attention_args(qkv, vT, out, H, segments)
+    _check(lib().zimg_attention_noalloc(_ptr(qkv), _ptr(vT), S_pad, _ptr(out), int(H), len(seg),
+                                        seg.ctypes.data_as(_I32P), _stream(stream)))
     return out
 
 

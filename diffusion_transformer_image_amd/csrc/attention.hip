@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace zimg {
 namespace {
 
@@ -440,7 +442,34 @@ __global__ __launch_bounds__(256) void attention_plan_kernel(AttnPlanArgs p) {
   }
 }
 
+// Scratch of the no-allocation entry point (see kernels.h): the work list
+// and the split partials of zimg_attention_noalloc.  Host code never passes
+// the array's name to a kernel (on the host it names a shadow, not the
+// device memory); kernels get the address hipGetSymbolAddress returns.
+__device__ __align__(256) unsigned char scratch[ATTN_SCRATCH_BYTES];
+
 }  // namespace
+
+void* attention_scratch(int device, hipError_t* err) {
+  static std::mutex mu;
+  static void* ptr[64] = {};
+  *err = hipSuccess;
+  if (device < 0 || device >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptr[device] = p;
+  }
+  return ptr[device];
+}
 
 hipError_t launch_attention_plan(const AttnPlanArgs& p, hipStream_t s) {
   if (p.B <= 0 || p.B > ATTN_OP_MAX_B) return hipErrorInvalidValue;

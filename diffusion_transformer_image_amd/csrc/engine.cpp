@@ -1623,6 +1623,25 @@ int zimg_attention(const void* qkv, const void* vT, int64_t S_pad, void* out, in
   return attention_op(qkv, vT, S_pad, out, H, B, seg, workspace, ws_bytes, (hipStream_t)stream);
 }
 
+// The same op with the library's static device scratch in place of a
+// workspace: nothing is allocated.  The scratch address of the current
+// device is looked up on its first use there (hipGetSymbolAddress, with that
+// device current) and kept.
+int zimg_attention_noalloc(const void* qkv, const void* vT, int64_t S_pad, void* out, int32_t H, int32_t B,
+                           const int32_t* seg, void* stream) {
+  g_last_error.clear();
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipError_t e = hipSuccess;
+  void* ws = zimg::attention_scratch(dev, &e);
+  if (!ws) return set_err(ZIMG_EHIP, "attention: device scratch of device %d unavailable: %s", dev, hipGetErrorString(e));
+  AttnOpPlan P;
+  int rc = attention_op_plan(H, B, seg, S_pad, zimg::ATTN_SCRATCH_BYTES, P);
+  if (rc) return set_err(rc, "attention (no-allocation entry point, %zu-byte scratch): %s", zimg::ATTN_SCRATCH_BYTES,
+                         g_last_error.c_str());
+  return attention_op(qkv, vT, S_pad, out, H, B, seg, ws, zimg::ATTN_SCRATCH_BYTES, (hipStream_t)stream);
+}
+
 // The flow-match schedule, in float64 and in the order of operations of the
 // definition: base sigmas as an evenly spaced ramp from 1 down to 1/N
 // (sigma_i = 1 + i * ((1/N - 1) / (N - 1)), the last one exactly 1/N), the

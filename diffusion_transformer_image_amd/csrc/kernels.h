@@ -179,6 +179,13 @@ struct AttnPlanArgs {
 };
 hipError_t launch_attention_plan(const AttnPlanArgs& p, hipStream_t s);
 
+// The device scratch of the no-allocation attention entry point: a
+// file-scope array of ATTN_SCRATCH_BYTES per GPU, its address looked up once
+// per device (with that device current) and kept.  Returns null and sets
+// *err on failure.
+constexpr size_t ATTN_SCRATCH_BYTES = (size_t)40 << 20;
+void* attention_scratch(int device, hipError_t* err);
+
 // ---------------------------------------------------------------- small ops
 // latent fp32 [B, C, Hp*p, Wp*p] -> tokens bf16, row b*npad + i*Wp + j, width p*p*C
 hipError_t launch_patchify(const float* latent, bf16_t* out, int B, int C, int Hp, int Wp,

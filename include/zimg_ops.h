@@ -198,6 +198,24 @@ int zimg_attention(const void* qkv, const void* vT, int64_t S_pad, void* out, in
                    const int32_t* seg, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * zimg_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation and arguments without the workspace.  The work list
+ * and split partials live in a static device array of
+ * ZIMG_ATTENTION_SCRATCH_BYTES (40 MiB) per GPU, which the library holds
+ * until the process ends; no call allocates or frees anything.  A problem
+ * whose work list does not fit fails with ZIMG_EINVAL; when the partials of
+ * the full split plan do not fit, fewer pairs are split.  Every call on a
+ * GPU shares that GPU's array and nothing in it needs to start at zero (each
+ * call writes its work list and partials before reading them), so calls
+ * that overlap on one GPU (other streams, other host threads) race: they
+ * must be ordered, e.g. on one stream.
+ */
+#define ZIMG_ATTENTION_SCRATCH_BYTES ((size_t)40 << 20)
+int zimg_attention_noalloc(const void* qkv, const void* vT, int64_t S_pad, void* out, int32_t H, int32_t B,
+                           const int32_t* seg, void* stream);
+
+/*
  * Attention work decomposition chosen for one stage (0: noise refiner, the
  * image rows; 1: context refiner, the caption rows; 2: joint blocks, all
  * rows) at the geometry of the most recent forward or run_blocks call on the

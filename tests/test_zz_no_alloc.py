@@ -1,0 +1,75 @@
+"""The no-allocation attention entry point (zimg_attention_noalloc) through
+the C ABI, against the workspace entry point (zimg_attention) on the same
+inputs: two calls in a row on the GPU's shared static scratch, the second
+with a smaller problem, each bitwise equal to the workspace entry point's
+output and within the parity bar of the oracle's attention."""
+
+import numpy as np
+import pytest
+
+from tests.test_gpu_attention_op import check, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _device(a):
+    torch = _torch()
+    import synthetic
+    return torch.from_numpy(synthetic.bf16_bits(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _both(qkv, vT, H, seg):
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    qkv_d, vT_d = _device(qkv), _device(vT)
+    out_ws = torch.zeros((qkv.shape[0], H * 128), dtype=torch.bfloat16, device="cuda")
+    out_na = torch.zeros_like(out_ws)
+    binding.attention(qkv_d, vT_d, out_ws, H, seg)
+    binding.attention_noalloc(qkv_d, vT_d, out_na, H, seg)
+    torch.cuda.synchronize()
+    return out_ws.float().cpu().numpy(), out_na.float().cpu().numpy()
+
+
+def test_noalloc_matches_workspace_entry_point_twice():
+    # first call: the 1024x1024 joint geometry (30 heads, 4,608 rows; the last
+    # round is split, so the scratch holds partials)
+    H1, N, L = 30, 4096, 512
+    seg1 = [(0, N, N, L)]
+    qkv1, vT1 = make_inputs(N + L, H1, N + L + 64, seed=11)
+    ws1, na1 = _both(qkv1, vT1, H1, seg1)
+    assert np.array_equal(ws1, na1), "first call: no-allocation output differs from the workspace entry point's"
+    r1, _ = check(na1, qkv1, H1, seg1, n_sample=32, seed=12)
+    # second call, smaller: three samples with mixed segments on the same scratch
+    H2, S_pad2 = 4, 448
+    seg2 = [(0, 120, 128, 77), (208, 5, 216, 0), (224, 64, 288, 65)]
+    qkv2, vT2 = make_inputs(360, H2, S_pad2, seed=13)
+    ws2, na2 = _both(qkv2, vT2, H2, seg2)
+    assert np.array_equal(ws2, na2), "second call: no-allocation output differs from the workspace entry point's"
+    r2, _ = check(na2, qkv2, H2, seg2)
+    print(f"no-allocation entry point: rel-L2 vs the oracle {r1:.2e} (1024 joint), {r2:.2e} (mixed segments)")
+
+
+def test_noalloc_rejects_a_work_list_beyond_the_scratch():
+    """64 samples of two 2^24-row ranges need a 268 MB work list, more than
+    the 40 MiB scratch: refused with an error that names the limit, before
+    anything is enqueued (the buffers are allocated but never read)."""
+    torch = _torch()
+    from diffusion_transformer_image_amd import binding
+    H, S_pad = 1, 1 << 24
+    qkv = torch.empty((S_pad, 3 * 128), dtype=torch.bfloat16, device="cuda")
+    vT = torch.empty((128, S_pad), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((S_pad, 128), dtype=torch.bfloat16, device="cuda")
+    seg = [(0, S_pad - 64, 0, S_pad - 64)] * 64
+    with pytest.raises(binding.ZimgError, match="no-allocation entry point, 41943040-byte scratch"):
+        binding.attention_noalloc(qkv, vT, out, H, seg)
+    # the workspace entry point states the size it would need instead
+    assert binding.attention_workspace_size(H, seg, S_pad) > 40 << 20
+    del qkv, vT, out
+    torch.cuda.empty_cache()
