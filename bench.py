@@ -136,7 +136,8 @@ def summarize(stats, steps, work, int8=False):
 
 def cpu_baseline(wl, model):
     """Time the float64 oracle on one joint block of the workload (all rows),
-    then scale to a whole forward by the algorithmic FLOP ratio."""
+    then scale to a whole forward by the algorithmic FLOP ratio (an
+    extrapolation, labelled as such, with the host CPU model and BLAS)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -158,7 +159,18 @@ def cpu_baseline(wl, model):
     cos, sin = om.rope_tables(cfg, np.concatenate([img_ids, cap_ids]))
     c = om.timestep_mlp(cfg, Wb, np.array([wl["t"][0]]))[0]
     mod = om.block_modulation(Wb, p, c)
-    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+    threads = max([d.get("num_threads", 1) for d in blas] or [1])
+    blas_name = ", ".join(sorted({f"{d.get('internal_api', '?')} {d.get('version', '')}".strip() for d in blas})) or "unknown"
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     t0 = time.perf_counter()
     om.block(cfg, Wb, p, x, cos, sin, mod)
     block_s = time.perf_counter() - t0
@@ -168,9 +180,10 @@ def cpu_baseline(wl, model):
     joint_flops = 2.0 * S * Dm * (4 * Dm + 3 * Fm) + 4.0 * S * S * Dm
     fwd_s = block_s * fwd_flops / joint_flops
     return {"value": round(S / fwd_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"one joint block (all {S} rows, hidden {Dm}) of the forward in float64 numpy, "
-                       f"{block_s:.2f} s; whole-forward time scaled by algorithmic FLOPs "
-                       f"({fwd_flops / joint_flops:.2f} x the block)")}
+            "cpu": cpu_model, "blas": blas_name, "precision": "float64",
+            "sample": (f"extrapolation: one float64 joint block of the forward (all {S} rows, hidden {Dm}) "
+                       f"timed at {block_s:.2f} s, scaled to the whole forward by the algorithmic FLOP ratio "
+                       f"({fwd_flops / joint_flops:.2f} x the block); the whole forward never ran on the CPU")}
 
 
 # ---------------------------------------------------------------- traffic from committed counters
