@@ -41,6 +41,10 @@ class ModelConfig:
     max_period: float = 10000.0
     norm_eps: float = 1e-5
     final_eps: float = 1e-6
+    # 0: each sample's sequence holds exactly its caption and image tokens
+    # ("padding dropped"); 32: each of the two runs is padded to a multiple
+    # of 32 with the learned x_pad_token / cap_pad_token (see model.py)
+    token_pad: int = 0
 
     @property
     def head_dim(self) -> int:

@@ -3,10 +3,17 @@
 Test infrastructure only (see oracle/__init__.py).
 
 Module names follow the ones the pages print: ``t_embedder``,
-``cap_embedder``, ``all_x_embedder`` (here ``x_embedder``) and
-``all_final_layer`` ([AIT] "Specifics", quantization note),
+``cap_embedder``, ``all_x_embedder`` and ``all_final_layer`` ([AIT]
+"Specifics", quantization note; the patch-size key ``2-1`` of both),
 ``final_layer.linear`` at [64, 3840] ([H3D] "What was changed, and why"),
-``to_out`` and the FFN's ``w1/w2/w3`` ([MNN] "Conversion details").
+``to_out`` and the FFN's ``w1/w2/w3`` ([MNN] "Conversion details").  The
+whole key set is pinned: its sorted-key SHA-256 equals the digest [FV]
+"Component contracts" (Transformer) prints for the released checkpoint's
+safetensors index, which also fixes the module order inside the small
+sequentials -- ``t_embedder.mlp.0`` / ``.2`` (an activation at index 1),
+``cap_embedder.0`` (the RMSNorm) before ``.1`` (the linear), a block's
+``adaLN_modulation.0`` (the linear first: no activation in front of it) and
+the final layer's ``adaLN_modulation.1`` (an activation at index 0).
 
 Block structure (the reading that reproduces the printed counts):
   * separate q, k, v, out projections without bias, QK-RMSNorm weights of
@@ -83,12 +90,12 @@ def manifest(cfg: ModelConfig):
         ("cap_embedder.0.weight", (cfg.cap_feat_dim,)),
         ("cap_embedder.1.weight", (D, cfg.cap_feat_dim)),
         ("cap_embedder.1.bias", (D,)),
-        ("x_embedder.weight", (D, cfg.patch_dim)),
-        ("x_embedder.bias", (D,)),
-        ("final_layer.adaLN_modulation.1.weight", (D, cfg.adaln_dim)),
-        ("final_layer.adaLN_modulation.1.bias", (D,)),
-        ("final_layer.linear.weight", (cfg.patch_dim, D)),
-        ("final_layer.linear.bias", (cfg.patch_dim,)),
+        ("all_x_embedder.2-1.weight", (D, cfg.patch_dim)),
+        ("all_x_embedder.2-1.bias", (D,)),
+        ("all_final_layer.2-1.adaLN_modulation.1.weight", (D, cfg.adaln_dim)),
+        ("all_final_layer.2-1.adaLN_modulation.1.bias", (D,)),
+        ("all_final_layer.2-1.linear.weight", (cfg.patch_dim, D)),
+        ("all_final_layer.2-1.linear.bias", (cfg.patch_dim,)),
         ("x_pad_token", (1, D)),
         ("cap_pad_token", (1, D)),
     ]

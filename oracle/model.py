@@ -303,7 +303,7 @@ def block(cfg: ModelConfig, W, prefix, x, cos, sin, mod=None, rows=None, taps=No
 def x_embed(cfg: ModelConfig, W, latent):
     """Patch embed: patchify 2x2 then linear patch_dim -> hidden with bias."""
     v = patchify(latent, cfg.patch)
-    return v @ _f64(W["x_embedder.weight"]).T + _f64(W["x_embedder.bias"])
+    return v @ _f64(W["all_x_embedder.2-1.weight"]).T + _f64(W["all_x_embedder.2-1.bias"])
 
 
 def cap_embed(cfg: ModelConfig, W, feats):
@@ -320,10 +320,42 @@ def final_layer(cfg: ModelConfig, W, x_img, c):
     final_layer.linear is [64, 3840].  Reading: SiLU in front of its
     modulation linear, a scale only, and LayerNorm without affine.
     """
-    scale = _f64(W["final_layer.adaLN_modulation.1.weight"]) @ silu(c) + _f64(
-        W["final_layer.adaLN_modulation.1.bias"])
+    scale = _f64(W["all_final_layer.2-1.adaLN_modulation.1.weight"]) @ silu(c) + _f64(
+        W["all_final_layer.2-1.adaLN_modulation.1.bias"])
     z = layer_norm(x_img, cfg.final_eps) * (1.0 + scale)
-    return z @ _f64(W["final_layer.linear.weight"]).T + _f64(W["final_layer.linear.bias"])
+    return z @ _f64(W["all_final_layer.2-1.linear.weight"]).T + _f64(W["all_final_layer.2-1.linear.bias"])
+
+
+def padded_sequence(cfg: ModelConfig, W, x_img, y, Hp, Wp):
+    """The sample's image and caption runs as the blocks see them, with
+    their 3-axis position ids: (x_img, y, ids_cap, ids_img).
+
+    cfg.token_pad = 0: the embedded tokens as they are ([AIT]
+    "Architecture": padding dropped), positions from ``position_ids``.
+    cfg.token_pad = p (32): the released model's padding ([H3D] "Measured
+    performance versus the regular layout": a 4,128 = 4,096 + 32 token
+    forward; [AIT] "Components": the parameter total includes the two
+    3840-d pad embeddings; [FV] "Component contracts", Transformer: the
+    padded variable-length stream needs a key mask).  Reading, parity
+    unpinned beyond that: each run is padded to a multiple of p, the image
+    run with copies of x_pad_token and the caption run with copies of
+    cap_pad_token; pad tokens are ordinary members of their sample's
+    sequence (queries and keys; only other samples are masked); the caption
+    positions continue through its pads (k + 1 for k < L_p), the image
+    positions start after the padded caption ((L_p + 1, i, j)), and image
+    pad tokens sit at position (0, 0, 0).
+    """
+    N, L = x_img.shape[0], y.shape[0]
+    p = cfg.token_pad
+    if not p:
+        ids_cap, ids_img = position_ids(L, Hp, Wp)
+        return x_img, y, ids_cap, ids_img
+    Np, Lp = -(-N // p) * p, -(-L // p) * p
+    x_img = np.concatenate([x_img, np.repeat(_f64(W["x_pad_token"]).reshape(1, -1), Np - N, axis=0)])
+    y = np.concatenate([y, np.repeat(_f64(W["cap_pad_token"]).reshape(1, -1), Lp - L, axis=0)])
+    ids_cap, ids_img = position_ids(Lp, Hp, Wp)
+    ids_img = np.concatenate([ids_img, np.zeros((Np - N, 3), dtype=np.int32)])
+    return x_img, y, ids_cap, ids_img
 
 
 def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak=None, quant=None):
@@ -345,11 +377,11 @@ def forward_sample(cfg: ModelConfig, W, latent, feats, t, capture=None, ffn_peak
 
     x_img = x_embed(cfg, W, latent)
     y = cap_embed(cfg, W, feats)
+    x_img, y, ids_cap, ids_img = padded_sequence(cfg, W, x_img, y, Hp, Wp)
     if capture is not None:
         capture["x_embed"] = x_img.copy()
         capture["cap_embed"] = y.copy()
 
-    ids_cap, ids_img = position_ids(L, Hp, Wp)
     cos_img, sin_img = rope_tables(cfg, ids_img)
     cos_cap, sin_cap = rope_tables(cfg, ids_cap)
     cos_all = np.concatenate([cos_img, cos_cap])

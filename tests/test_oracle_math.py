@@ -349,17 +349,17 @@ def test_forward_small_batch_and_finiteness():
 def test_final_layer_by_hand():
     cfg = ModelConfig(hidden=4, n_heads=1, adaln_dim=2)
     rng = np.random.default_rng(11)
-    W = {"final_layer.adaLN_modulation.1.weight": rng.standard_normal((4, 2)),
-         "final_layer.adaLN_modulation.1.bias": rng.standard_normal(4),
-         "final_layer.linear.weight": rng.standard_normal((3, 4)),
-         "final_layer.linear.bias": rng.standard_normal(3)}
+    W = {"all_final_layer.2-1.adaLN_modulation.1.weight": rng.standard_normal((4, 2)),
+         "all_final_layer.2-1.adaLN_modulation.1.bias": rng.standard_normal(4),
+         "all_final_layer.2-1.linear.weight": rng.standard_normal((3, 4)),
+         "all_final_layer.2-1.linear.bias": rng.standard_normal(3)}
     x = rng.standard_normal((1, 4))
     c = rng.standard_normal(2)
-    sc = W["final_layer.adaLN_modulation.1.weight"] @ (c / (1 + np.exp(-c))) + W["final_layer.adaLN_modulation.1.bias"]
+    sc = W["all_final_layer.2-1.adaLN_modulation.1.weight"] @ (c / (1 + np.exp(-c))) + W["all_final_layer.2-1.adaLN_modulation.1.bias"]
     mu = x[0].sum() / 4
     var = ((x[0] - mu) ** 2).sum() / 4
     z = (x[0] - mu) / math.sqrt(var + 1e-6) * (1 + sc)
-    ref = W["final_layer.linear.weight"] @ z + W["final_layer.linear.bias"]
+    ref = W["all_final_layer.2-1.linear.weight"] @ z + W["all_final_layer.2-1.linear.bias"]
     np.testing.assert_allclose(om.final_layer(cfg, W, x, c)[0], ref, rtol=1e-12)
 
 

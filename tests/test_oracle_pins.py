@@ -322,3 +322,64 @@ def test_modulated_block_by_hand_rejects_mutants(monkeypatch):
     with monkeypatch.context() as mp:
         mp.setattr(om, "block", _mutant(om.block, norm_first, rope_first))
         assert not passes()
+
+
+# ---------------------------------------------------------------- pad tokens
+
+def test_padded_sequence_by_hand():
+    """token_pad 32: an image run of 5 and a caption run of 3 tokens become
+    32 + 32 rows; the added rows are copies of x_pad_token / cap_pad_token;
+    caption positions run 1..32, real image tokens sit at (33, i, j), image
+    pads at (0, 0, 0).  token_pad 0 leaves the runs and positions alone."""
+    D = 8
+    rng = np.random.default_rng(30)
+    W = {"x_pad_token": rng.standard_normal((1, D)), "cap_pad_token": rng.standard_normal((1, D))}
+    x_img, y = rng.standard_normal((5, D)), rng.standard_normal((3, D))
+    cfg = ModelConfig(hidden=D, n_heads=1, token_pad=32)
+    xi, yy, ids_cap, ids_img = om.padded_sequence(cfg, W, x_img, y, 1, 5)
+    assert xi.shape == (32, D) and yy.shape == (32, D)
+    assert np.array_equal(xi[:5], x_img) and np.array_equal(yy[:3], y)
+    for r in range(5, 32):
+        assert np.array_equal(xi[r], W["x_pad_token"][0])
+    for r in range(3, 32):
+        assert np.array_equal(yy[r], W["cap_pad_token"][0])
+    assert ids_cap.tolist() == [[k + 1, 0, 0] for k in range(32)]
+    assert ids_img.tolist() == [[33, 0, j] for j in range(5)] + [[0, 0, 0]] * 27
+    cfg0 = ModelConfig(hidden=D, n_heads=1)
+    xi0, yy0, c0, i0 = om.padded_sequence(cfg0, W, x_img, y, 1, 5)
+    assert xi0 is x_img and yy0 is y
+    assert c0.tolist() == [[1, 0, 0], [2, 0, 0], [3, 0, 0]] and i0.tolist() == [[4, 0, j] for j in range(5)]
+
+
+def _tiny_forward(token_pad, lat_shape, L, W=None, seed=3):
+    import synthetic
+    from oracle import manifest
+    cfg = ModelConfig(hidden=256, n_heads=2, ffn=384, n_layers=1, n_noise_refiner=1, n_context_refiner=1,
+                      cap_feat_dim=64, t_mid=64, token_pad=token_pad)
+    if W is None:
+        W = synthetic.SyntheticWeights(manifest(cfg), seed=seed).materialize(workers=2)
+    lat = synthetic.latent(lat_shape, seed=seed)
+    caps = synthetic.captions((L,), dim=64, seed=seed)
+    return om.forward(cfg, W, lat, caps, np.array([0.4])), W
+
+
+def test_padding_is_a_no_op_on_whole_runs():
+    """Runs that already hold a multiple of 32 tokens get no pad tokens:
+    the padded forward is the plain one, bit for bit."""
+    a, W = _tiny_forward(32, (1, 16, 8, 16), 32)    # 4 x 8 = 32 image tokens, 32 caption tokens
+    b, _ = _tiny_forward(0, (1, 16, 8, 16), 32, W)
+    assert np.array_equal(a, b)
+
+
+def test_pad_tokens_take_part_in_attention():
+    """With ragged runs the pad embeddings reach the real tokens' outputs
+    (they are keys of the sample): changing either pad token changes the
+    output, and the padded forward differs from the plain one."""
+    a, W = _tiny_forward(32, (1, 16, 6, 10), 7)     # 15 image tokens -> 32, 7 caption tokens -> 32
+    plain, _ = _tiny_forward(0, (1, 16, 6, 10), 7, W)
+    assert not np.allclose(a, plain, rtol=1e-3)
+    for key in ("x_pad_token", "cap_pad_token"):
+        W2 = dict(W)
+        W2[key] = W[key] + 0.5
+        b, _ = _tiny_forward(32, (1, 16, 6, 10), 7, W2)
+        assert np.all(np.isfinite(b)) and not np.allclose(a, b, rtol=1e-6), key

@@ -22,12 +22,26 @@ def test_key_count_matches_page(golden):
     assert len(set(keys)) == len(keys)
 
 
+def test_key_set_digest_matches_page(golden):
+    """The 521 names, sorted, newline-terminated, hash (SHA-256) to the digest
+    the FastVideo handoff prints for the released checkpoint's index: every
+    name, including the module indexes that fix where the activations sit,
+    is the released model's."""
+    import hashlib
+    keys = sorted(k for k, _ in manifest(ModelConfig()))
+    digest = hashlib.sha256("".join(k + "\n" for k in keys).encode()).hexdigest()
+    assert digest == golden["page_constants"]["checkpoint_key_digest"]["value"]
+    # a single renamed key changes it
+    bad = sorted(keys[:-1] + ["layers.29.feed_forward.w4.weight"])
+    assert hashlib.sha256("".join(k + "\n" for k in bad).encode()).hexdigest() != digest
+
+
 def test_final_layer_size(golden):
     pc = golden["page_constants"]
     m = dict(manifest(ModelConfig()))
-    fl = sum(_n(s) for k, s in m.items() if k.startswith("final_layer."))
+    fl = sum(_n(s) for k, s in m.items() if k.startswith("all_final_layer.2-1."))
     assert abs(fl - pc["final_layer_params"]["value"]) <= pc["final_layer_params"]["rel_tol"] * 1.2e6
-    assert list(m["final_layer.linear.weight"]) == pc["final_layer_linear_shape"]["value"]
+    assert list(m["all_final_layer.2-1.linear.weight"]) == pc["final_layer_linear_shape"]["value"]
 
 
 def test_storage_sizes(golden):
