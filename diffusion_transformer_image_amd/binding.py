@@ -47,7 +47,7 @@ class Config(ctypes.Structure):
         ("t_scale", ctypes.c_float), ("max_period", ctypes.c_float), ("norm_eps", ctypes.c_float),
         ("final_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_image_tokens", ctypes.c_int32), ("max_caption_tokens", ctypes.c_int32),
-        ("batch_invariant", ctypes.c_int32), ("linear_int8", ctypes.c_int32),
+        ("batch_invariant", ctypes.c_int32), ("linear_int8", ctypes.c_int32), ("token_pad", ctypes.c_int32),
     ]
 
     def as_dict(self):
@@ -85,6 +85,11 @@ SIGNATURES = {
     "zimg_dit_finalize": (_I32, [_P]),
     "zimg_dit_forward": (_I32, [_P, _P, _I32, _I32, _I32, _P, _I32, _I32P, _F32P, _P, _P]),
     "zimg_dit_destroy": (None, [_P]),
+    "zimg_safetensors_check": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_char_p), _I32, _I32P]),
+    "zimg_dit_load_safetensors": (_I32, [_P, ctypes.POINTER(ctypes.c_char_p), _I32]),
+    "zimg_dit_create_from_safetensors": (_I32, [ctypes.POINTER(Config), ctypes.POINTER(ctypes.c_char_p), _I32, _P,
+                                                ctypes.POINTER(_P)]),
+    "zimg_dit_manifest_digest": (_I32, [ctypes.POINTER(Config), ctypes.c_char_p]),
     "zimg_dit_last_error": (ctypes.c_char_p, [_P]),
     "zimg_dit_set_capture": (_I32, [_P, _P, ctypes.c_size_t]),
     "zimg_position_ids": (_I32, [_I32, _I32, _I32, _I32P, _I32P]),
@@ -118,6 +123,15 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m diffusion_transformer_image_amd.build` (there is no fallback)")
+        # One HIP runtime per process: PyTorch ships its own libamdhip64 (same
+        # soname as the one the library is linked against).  Loaded first, it
+        # is the one the library's dependency resolves to; loaded second, a
+        # second runtime would come up beside the library's and, on some
+        # hosts, find no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)
@@ -164,6 +178,29 @@ def manifest(cfg):
         _check(lib().zimg_dit_manifest_entry(ctypes.byref(cfg), i, ctypes.byref(name), ctypes.byref(nd), shp))
         out.append((name.value.decode(), tuple(shp[:nd.value])))
     return out
+
+
+def _paths(paths):
+    if isinstance(paths, (str, bytes, os.PathLike)):
+        paths = [paths]
+    enc = [os.fsencode(p) for p in paths]
+    return (ctypes.c_char_p * len(enc))(*enc), len(enc)
+
+
+def safetensors_check(cfg, paths):
+    """Validate safetensors files against the config's weight table
+    (zimg_safetensors_check); returns the tensor count."""
+    arr, n = _paths(paths)
+    cnt = ctypes.c_int32()
+    _check(lib().zimg_safetensors_check(ctypes.byref(cfg), arr, n, ctypes.byref(cnt)))
+    return cnt.value
+
+
+def manifest_digest(cfg):
+    """SHA-256 of the sorted weight names (zimg_dit_manifest_digest)."""
+    buf = ctypes.create_string_buffer(65)
+    _check(lib().zimg_dit_manifest_digest(ctypes.byref(cfg), buf))
+    return buf.value.decode()
 
 
 def _tensor(name, arr):
@@ -265,6 +302,18 @@ class DiT:
             self.close()
             raise
         self._capture = None
+
+    @classmethod
+    def from_safetensors(cls, cfg, paths, stream=None):
+        """An engine whose weights come from safetensors files
+        (zimg_dit_create_from_safetensors)."""
+        self = cls.__new__(cls)
+        self.cfg = cfg
+        self._h = ctypes.c_void_p()
+        self._capture = None
+        arr, n = _paths(paths)
+        _check(lib().zimg_dit_create_from_safetensors(ctypes.byref(cfg), arr, n, _stream(stream), ctypes.byref(self._h)))
+        return self
 
     def close(self):
         if self._h:

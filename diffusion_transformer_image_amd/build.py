@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzimg_dit.so")
-SOURCES = ["engine.cpp", "gemm.hip", "norm.hip", "attention.hip", "misc.hip"]
+SOURCES = ["engine.cpp", "loader.cpp", "gemm.hip", "norm.hip", "attention.hip", "misc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed-fp32 instructions are disabled on purpose (plain fp32 code only)

@@ -45,6 +45,17 @@ int set_err(int code, const char* fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+namespace zimg {
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+}  // namespace zimg
+
+namespace {
+
 #define HIP_TRY(expr)                                                                  \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
@@ -119,12 +130,12 @@ std::vector<ManifestEntry> build_manifest(const zimg_dit_config& c) {
   add("cap_embedder.0.weight", {c.cap_feat_dim});
   add("cap_embedder.1.weight", {D, c.cap_feat_dim});
   add("cap_embedder.1.bias", {D});
-  add("x_embedder.weight", {D, P});
-  add("x_embedder.bias", {D});
-  add("final_layer.adaLN_modulation.1.weight", {D, c.adaln_dim});
-  add("final_layer.adaLN_modulation.1.bias", {D});
-  add("final_layer.linear.weight", {P, D});
-  add("final_layer.linear.bias", {P});
+  add("all_x_embedder.2-1.weight", {D, P});
+  add("all_x_embedder.2-1.bias", {D});
+  add("all_final_layer.2-1.adaLN_modulation.1.weight", {D, c.adaln_dim});
+  add("all_final_layer.2-1.adaLN_modulation.1.bias", {D});
+  add("all_final_layer.2-1.linear.weight", {P, D});
+  add("all_final_layer.2-1.linear.bias", {P});
   add("x_pad_token", {1, D});
   add("cap_pad_token", {1, D});
   for (const auto& b : block_specs(c)) {
@@ -154,8 +165,8 @@ std::vector<ManifestEntry> build_manifest(const zimg_dit_config& c) {
 // life of the process; the cache may be reached from several threads (a
 // manifest query while another thread creates an engine), hence the lock.
 // Entries are never removed, so a returned reference stays valid unlocked.
-// (the key is the config's bytes: 24 four-byte fields, no padding)
-static_assert(sizeof(zimg_dit_config) == 24 * 4, "zimg_dit_config must have no padding");
+// (the key is the config's bytes: 25 four-byte fields, no padding)
+static_assert(sizeof(zimg_dit_config) == 25 * 4, "zimg_dit_config must have no padding");
 const std::vector<ManifestEntry>& cached_manifest(const zimg_dit_config& c) {
   static std::mutex mu;
   static std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>> cache;
@@ -200,6 +211,7 @@ int check_config(const zimg_dit_config* c) {
     return set_err(ZIMG_EUNSUPPORTED, "max_caption_tokens must be 1..512 (the caption limit of the model)");
   if (c->batch_invariant != 0 && c->batch_invariant != 1) return set_err(ZIMG_EINVAL, "batch_invariant must be 0 or 1");
   if (c->linear_int8 != 0 && c->linear_int8 != 1) return set_err(ZIMG_EINVAL, "linear_int8 must be 0 or 1");
+  if (c->token_pad != 0 && c->token_pad != 32) return set_err(ZIMG_EUNSUPPORTED, "token_pad must be 0 or 32");
   return ZIMG_OK;
 }
 
@@ -243,17 +255,20 @@ void rope_rows(const double* omega, const int* axis, const int32_t* ids, int64_t
 
 // ------------------------------------------------------------------ layout
 
-// Rows of the batch: sample b's image tokens (N[b] = Hp[b] * Wp[b], padded
-// to Npad[b], a multiple of 16) from img_off[b], all samples' image rows
-// first, then each caption padded to a multiple of 16 from cap_off[b].
+// Rows of the batch: sample b's image run from img_off[b] -- its N[b] =
+// Hp[b] * Wp[b] tokens, then with token padding the pad tokens up to Nseq[b]
+// (a multiple of the pad size; else Nseq = N) -- padded with rows outside
+// every sequence to Npad[b], a multiple of 16; all samples' image rows
+// first, then each caption run (lens[b] tokens, Lseq[b] with its pad
+// tokens) padded to a multiple of 16 from cap_off[b].
 struct Layout {
   int B = 0;
-  std::vector<int> Hl, Wl, Hp, Wp, N, Npad, lens, img_off, cap_off;
+  std::vector<int> Hl, Wl, Hp, Wp, N, Nseq, Npad, lens, Lseq, img_off, cap_off;
   int cap_base = 0, S = 0, Lsum = 0;
   bool uniform = true;  // every sample has the same latent size
 };
 
-Layout make_layout(int B, const int32_t* Hl, const int32_t* Wl, int patch, const int32_t* lens) {
+Layout make_layout(int B, const int32_t* Hl, const int32_t* Wl, int patch, const int32_t* lens, int token_pad = 0) {
   Layout L;
   L.B = B;
   int off = 0;
@@ -263,7 +278,8 @@ Layout make_layout(int B, const int32_t* Hl, const int32_t* Wl, int patch, const
     L.Hp.push_back(Hl[b] / patch);
     L.Wp.push_back(Wl[b] / patch);
     L.N.push_back(L.Hp[b] * L.Wp[b]);
-    L.Npad.push_back((int)round_up(L.N[b], 16));
+    L.Nseq.push_back(token_pad ? (int)round_up(L.N[b], token_pad) : L.N[b]);
+    L.Npad.push_back((int)round_up(L.Nseq[b], 16));
     L.img_off.push_back(off);
     off += L.Npad[b];
     L.uniform = L.uniform && Hl[b] == Hl[0] && Wl[b] == Wl[0];
@@ -271,17 +287,18 @@ Layout make_layout(int B, const int32_t* Hl, const int32_t* Wl, int patch, const
   L.cap_base = off;
   for (int b = 0; b < B; ++b) {
     L.lens.push_back(lens[b]);
+    L.Lseq.push_back(token_pad ? (int)round_up(lens[b], token_pad) : lens[b]);
     L.cap_off.push_back(off);
-    off += (int)round_up(lens[b], 16);
+    off += (int)round_up(L.Lseq[b], 16);
     L.Lsum += lens[b];
   }
   L.S = off;
   return L;
 }
 
-Layout make_layout(int B, int Hl, int Wl, int patch, const int32_t* lens) {
+Layout make_layout(int B, int Hl, int Wl, int patch, const int32_t* lens, int token_pad = 0) {
   std::vector<int32_t> hv(B, Hl), wv(B, Wl);
-  return make_layout(B, hv.data(), wv.data(), patch, lens);
+  return make_layout(B, hv.data(), wv.data(), patch, lens, token_pad);
 }
 
 // True when the B per-sample buffers of a one-size batch are consecutive
@@ -548,12 +565,12 @@ int zimg_dit::allocate() {
   vec("cap_embedder.0.weight", capn_w, c.cap_feat_dim);
   mat("cap_embedder.1.weight", cap_w, D, c.cap_feat_dim);
   vec("cap_embedder.1.bias", cap_b, D);
-  mat("x_embedder.weight", x_w, D, P);
-  vec("x_embedder.bias", x_b, D);
-  mat("final_layer.adaLN_modulation.1.weight", ada_w + (int64_t)n_mod * 4 * D * c.adaln_dim, D, c.adaln_dim);
-  vec("final_layer.adaLN_modulation.1.bias", ada_b + (int64_t)n_mod * 4 * D, D);
-  mat("final_layer.linear.weight", fin_w, P, D);
-  vec("final_layer.linear.bias", fin_b, P);
+  mat("all_x_embedder.2-1.weight", x_w, D, P);
+  vec("all_x_embedder.2-1.bias", x_b, D);
+  mat("all_final_layer.2-1.adaLN_modulation.1.weight", ada_w + (int64_t)n_mod * 4 * D * c.adaln_dim, D, c.adaln_dim);
+  vec("all_final_layer.2-1.adaLN_modulation.1.bias", ada_b + (int64_t)n_mod * 4 * D, D);
+  mat("all_final_layer.2-1.linear.weight", fin_w, P, D);
+  vec("all_final_layer.2-1.linear.bias", fin_b, P);
   vec("x_pad_token", pad_x, D);
   vec("cap_pad_token", pad_cap, D);
   for (size_t i = 0; i < blocks.size(); ++i) {
@@ -580,8 +597,9 @@ int zimg_dit::allocate() {
   }
 
   // workspace
-  img_rows_max = (int64_t)c.max_batch * round_up(c.max_image_tokens, 16);
-  cap_rows_max = (int64_t)c.max_batch * round_up(c.max_caption_tokens, 16);
+  const int row_align = c.token_pad ? std::max(16, (int)c.token_pad) : 16;
+  img_rows_max = (int64_t)c.max_batch * round_up(c.max_image_tokens, row_align);
+  cap_rows_max = (int64_t)c.max_batch * round_up(c.max_caption_tokens, row_align);
   S_max = img_rows_max + cap_rows_max;
   S_pad = round_up(S_max, 64) + 64;
   ALLOC(x, S_max * D);
@@ -756,13 +774,16 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
     rope_freqs(c, omega, axis);
     std::vector<int32_t> cap_ids, img_ids;
     for (int b = 0; b < L.B; ++b) {
-      cap_ids.assign((size_t)L.lens[b] * 3, 0);
+      // positions of the caption run (with its pad tokens, which continue it)
+      // and of the image tokens after it; image pad tokens keep the
+      // identity rows (position 0) the tables were cleared to
+      cap_ids.assign((size_t)L.Lseq[b] * 3, 0);
       img_ids.assign((size_t)L.N[b] * 3, 0);
-      position_ids(L.lens[b], L.Hp[b], L.Wp[b], cap_ids.data(), img_ids.data());
+      position_ids(L.Lseq[b], L.Hp[b], L.Wp[b], cap_ids.data(), img_ids.data());
       rope_rows(omega, axis, img_ids.data(), L.N[b], cs + (int64_t)L.img_off[b] * 64, sn + (int64_t)L.img_off[b] * 64);
-      rope_rows(omega, axis, cap_ids.data(), L.lens[b], cs + (int64_t)L.cap_off[b] * 64, sn + (int64_t)L.cap_off[b] * 64);
+      rope_rows(omega, axis, cap_ids.data(), L.Lseq[b], cs + (int64_t)L.cap_off[b] * 64, sn + (int64_t)L.cap_off[b] * 64);
       for (int i = 0; i < L.Npad[b]; ++i) rs[L.img_off[b] + i] = b;
-      for (int i = 0; i < (int)round_up(L.lens[b], 16); ++i) rs[L.cap_off[b] + i] = b;
+      for (int i = 0; i < (int)round_up(L.Lseq[b], 16); ++i) rs[L.cap_off[b] + i] = b;
     }
     // segments and q-tiles of 128 rows per stage
     for (int stg = 0; stg < 3; ++stg) {
@@ -773,11 +794,11 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
         int k = 0;
         if (stg != 1) {
           q.r0[k] = L.img_off[b];
-          q.n[k++] = L.N[b];
+          q.n[k++] = L.Nseq[b];
         }
         if (stg != 0) {
           q.r0[k] = L.cap_off[b];
-          q.n[k++] = L.lens[b];
+          q.n[k++] = L.Lseq[b];
         }
         for (int r = 0; r < k; ++r)
           for (int q0 = 0; q0 < q.n[r]; q0 += 128) {
@@ -1039,6 +1060,12 @@ int zimg_dit::forward(const float* const* latents, const Layout& L, const void* 
   ga.ep.C = x + (int64_t)L.cap_base * D;
   ga.ep.bias = cap_b;
   HIP_TRY(zimg::launch_gemm(ga, s));
+  // pad tokens: the learned embeddings replace whatever the embed GEMMs left
+  // in those rows
+  for (int b = 0; b < L.B; ++b) {
+    HIP_TRY(zimg::launch_set_rows(x, D, pad_x, L.img_off[b] + L.N[b], L.Nseq[b] - L.N[b], s));
+    HIP_TRY(zimg::launch_set_rows(x, D, pad_cap, L.cap_off[b] + L.lens[b], L.Lseq[b] - L.lens[b], s));
+  }
   rc = prof_stop(s);
   if (rc) return rc;
   const size_t slot_bytes = (size_t)L.S * D * 4;
@@ -1155,7 +1182,7 @@ int run_forward(zimg_dit* h, const float* const* latents, int32_t B, const int32
   for (int b = 0; b < B; ++b)
     if (!latents[b] || !outs[b]) return set_err(ZIMG_EINVAL, "latent and output buffers must be non-NULL");
   if (cap_dtype != ZIMG_F32 && cap_dtype != ZIMG_BF16) return set_err(ZIMG_EINVAL, "cap_dtype must be ZIMG_F32 or ZIMG_BF16");
-  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
+  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens, h->cfg.token_pad);
   if (h->cap_buf) {
     const size_t need = (size_t)(h->blocks.size() + 1) * L.S * h->cfg.hidden * 4;
     if (h->cap_bytes < need) return set_err(ZIMG_EINVAL, "capture buffer has %zu bytes, needs %zu", h->cap_bytes, need);
@@ -1263,6 +1290,11 @@ int attention_op(const void* qkv, const void* vT, int64_t S_pad, void* out, int3
 
 }  // namespace
 
+namespace zimg {
+const zimg_dit_config* handle_config(const zimg_dit* h) { return h ? &h->cfg : nullptr; }
+bool handle_finalized(const zimg_dit* h) { return h && h->finalized; }
+}  // namespace zimg
+
 extern "C" {
 
 const char* zimg_last_error(void) { return g_last_error.c_str(); }
@@ -1291,6 +1323,7 @@ void zimg_dit_default_config(zimg_dit_config* c) {
   c->final_eps = 1e-6f;
   c->max_batch = 1;
   c->max_image_tokens = 4096;
+  c->token_pad = 0;
   c->max_caption_tokens = 512;
 }
 
@@ -1423,7 +1456,7 @@ int zimg_dit_run_blocks(zimg_dit* h, float* x_io, int32_t B, int32_t Hl, int32_t
   if (first_block < 0 || n_blocks < 1 || first_block + n_blocks > (int32_t)h->blocks.size())
     return h->fail(set_err(ZIMG_EINVAL, "blocks [%d, %d) out of range 0..%zu", first_block, first_block + n_blocks,
                            h->blocks.size()));
-  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens);
+  Layout L = make_layout(B, Hl, Wl, h->cfg.patch, caption_lens, h->cfg.token_pad);
   rc = h->run_blocks(x_io, L, t, first_block, n_blocks, (hipStream_t)stream);
   return rc ? h->fail(rc) : ZIMG_OK;
 }

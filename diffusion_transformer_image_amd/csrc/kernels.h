@@ -206,5 +206,7 @@ hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g,
                             hipStream_t s);
 // fill n floats with v
 hipError_t launch_fill(float* p, float v, int64_t n, hipStream_t s);
+// rows [r0, r0 + n) of x (row length and stride D) = v[0 .. D)
+hipError_t launch_set_rows(float* x, int D, const float* v, int r0, int n, hipStream_t s);
 
 }  // namespace zimg

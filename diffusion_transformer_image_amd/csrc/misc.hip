@@ -100,6 +100,12 @@ __global__ void cfg_euler_kernel(float* x, const float* oc, const float* ou, flo
   if (i < n) x[i] = fmaf(dt, -fmaf(g, oc[i] - ou[i], oc[i]), x[i]);
 }
 
+// one workgroup per row: x[row][d] = v[d]
+__global__ __launch_bounds__(256) void set_rows_kernel(float* x, int D, const float* __restrict__ v) {
+  float* row = x + (int64_t)blockIdx.x * D;
+  for (int d = threadIdx.x; d < D; d += 256) row[d] = v[d];
+}
+
 __global__ void fill_kernel(float* p, float v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -141,6 +147,12 @@ hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g,
                        (const float4*)oc, (const float4*)ou, g, dt, n / 4);
   else
     hipLaunchKernelGGL(cfg_euler_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, x, oc, ou, g, dt, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_rows(float* x, int D, const float* v, int r0, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(set_rows_kernel, dim3(n), dim3(256), 0, s, x + (int64_t)r0 * D, D, v);
   return hipGetLastError();
 }
 

@@ -94,6 +94,21 @@ typedef struct zimg_dit_config {
                                 Turbo MNN (int8, fp16-safe)", Conversion details: 8-bit
                                 weights; "Z-Image" (AI Toolkit docs), Specifics: the
                                 embedders and final layer are not quantized) */
+  int32_t token_pad;         /* 0 (default): a sample's sequence holds exactly its image
+                                and caption tokens ("Z-Image" (AI Toolkit docs),
+                                Architecture: padding dropped).  32: each of the two runs
+                                is padded to a multiple of 32 with the learned
+                                x_pad_token / cap_pad_token, which take part in the
+                                sample's attention like its other tokens; caption
+                                positions continue through the pads, image positions
+                                start after the padded caption, image pads sit at
+                                position (0, 0, 0) ("Z-Image-Turbo, repackaged for
+                                H3ddle", Measured performance: a 4,096 + 32 token
+                                forward; "Local component coverage and quality handoff
+                                for the zimage FastVideo port", Transformer: the padded
+                                stream needs a key mask).  The row layout is then the
+                                one of the padded counts (zimg_row_layout with each
+                                count rounded up to 32). */
 } zimg_dit_config;
 
 /* One named weight tensor handed to the engine.  ``data`` is a HOST
@@ -189,6 +204,40 @@ int zimg_dit_forward(zimg_dit* h, const float* latent, int32_t B, int32_t Hl, in
 int zimg_dit_forward_varsize(zimg_dit* h, const float* const* latents, int32_t B, const int32_t* Hl,
                              const int32_t* Wl, const void* caption_feats, int32_t cap_dtype,
                              const int32_t* caption_lens, const float* t, float* const* outs, void* stream);
+
+/*
+ * Weights from safetensors files ("Local component coverage and quality
+ * handoff for the zimage FastVideo port", Component contracts: loading
+ * accounts for every parameter and ignores nothing; "Z-Image" (AI Toolkit
+ * docs), Specifics: one .safetensors file of the transformer).  ``paths``
+ * (HOST, n_paths file names) together must hold exactly the tensors of the
+ * config's weight table (zimg_dit_manifest_entry), each once, with the
+ * table's shape, dtype F32 or BF16, and data_offsets inside the file and
+ * matching the shape; "__metadata__" (string values only) is allowed.
+ * Everything is validated before any tensor is uploaded: ZIMG_EWEIGHT for a
+ * malformed file or a missing, unknown, duplicate or mis-shaped tensor,
+ * ZIMG_EUNSUPPORTED for another dtype, ZIMG_EINVAL for a file that cannot
+ * be opened.  The files are memory-mapped read-only and unmapped on return.
+ *   zimg_safetensors_check: the validation alone (no GPU needed);
+ *     *n_tensors (may be NULL) receives the tensor count.
+ *   zimg_dit_load_safetensors: into a handle from zimg_dit_alloc (then
+ *     zimg_dit_finalize); on failure the handle's weights are incomplete.
+ *   zimg_dit_create_from_safetensors: alloc + load + finalize (on failure
+ *     *out is NULL and nothing stays allocated).
+ */
+int zimg_safetensors_check(const zimg_dit_config* cfg, const char* const* paths, int32_t n_paths,
+                           int32_t* n_tensors);
+int zimg_dit_load_safetensors(zimg_dit* h, const char* const* paths, int32_t n_paths);
+int zimg_dit_create_from_safetensors(const zimg_dit_config* cfg, const char* const* paths, int32_t n_paths,
+                                     void* stream, zimg_dit** out);
+
+/* SHA-256 of the config's weight names sorted bytewise, each followed by a
+ * newline, as 64 lowercase hex digits and a NUL in ``hex`` (HOST, 65 bytes).
+ * For the full model this is the sorted key digest the FastVideo handoff
+ * ("Local component coverage and quality handoff for the zimage FastVideo
+ * port", Component contracts, Transformer) states for the released
+ * checkpoint's safetensors index. */
+int zimg_dit_manifest_digest(const zimg_dit_config* cfg, char hex[65]);
 
 /* Release all device and host memory of the handle (NULL is a no-op). */
 void zimg_dit_destroy(zimg_dit* h);

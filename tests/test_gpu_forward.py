@@ -237,10 +237,10 @@ def test_weight_table_errors():
     assert ei.value.code == binding.ZIMG_EWEIGHT and "duplicate" in str(ei.value)
     # mis-shaped
     bad = dict(W)
-    bad["x_embedder.weight"] = W["x_embedder.weight"][:, :32].copy()
+    bad["all_x_embedder.2-1.weight"] = W["all_x_embedder.2-1.weight"][:, :32].copy()
     with pytest.raises(binding.ZimgError) as ei:
         binding.DiT(ecfg, bad)
-    assert ei.value.code == binding.ZIMG_EWEIGHT and "x_embedder.weight" in str(ei.value)
+    assert ei.value.code == binding.ZIMG_EWEIGHT and "all_x_embedder.2-1.weight" in str(ei.value)
     # fp32 and bf16-bit inputs give the same engine
     binding.DiT(ecfg, W).close()
 
@@ -280,3 +280,4 @@ def test_geometry_switches_reuse_cached_tables():
     assert dit2.attention_plan(2) == plan_last
     dit.close()
     dit2.close()
+
