@@ -10,7 +10,7 @@
 //
 // Workgroup = 4 waves = 128 queries of one head; each wave owns 32 queries.
 // Keys stream through LDS in tiles of 64 (K as [key][128], V as the
-// transposed [128][key] tile read from vT) by direct global->LDS loads, K
+// transposed [128][key] tile read from vT) by direct buffer->LDS loads, K
 // into three buffers (loaded three tiles ahead) and V^T into two; scores of
 // the next tile are computed while the current tile's softmax runs, so
 // matrix-core and vector work overlap.
@@ -120,34 +120,38 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // V^T: chunk p -> row d = p/8, stored position p%8 holds keys 8*((p%8) ^ ((d>>1)&7)).
   // With p = (4 i + wave) * 64 + lane these reduce to: K load i fetches key
   // 16 i + kk0 at chunk hc, V^T load i fetches row 32 i + dd0 at key chunk kc,
-  // where kk0, hc, dd0, kc depend on the lane only -- so each lane keeps one
-  // 32-bit offset per operand and the per-tile address work is scalar.
+  // where kk0, hc, dd0, kc depend on the lane only -- so each lane keeps
+  // fixed 32-bit offsets per operand and the per-tile address work is scalar.
   const int r0 = wave * 4 + (lane >> 4);
   const int kk0 = swap_bits23(r0), hc = (lane & 15) ^ r0;
-  const uint32_t koff0 = (uint32_t)(kk0 * (int)ld + hc * 8);
+  uint32_t koff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)(((16 * i + kk0) * (int)ld + hc * 8) * 2);
   const int dd0 = wave * 8 + (lane >> 3);
   const uint32_t voff0 = (uint32_t)(dd0 * a.S_pad + (((lane & 7) ^ ((dd0 >> 1) & 7)) << 3));
+  // K tiles are read through a buffer resource that spans this head's K
+  // columns from the tile's first row to the last row of the buffer (at
+  // most one tile): key rows past the end of qkv read as zero instead of
+  // faulting, so every tile is loaded the same way, with no per-lane clamp
+  // and no branch (keys past a range's end are masked before the softmax).
+  const int64_t head_off = (int64_t)D + h * HD;
   auto dma_k = [&](int t, bf16_t* kb) {
-    const int kr0 = tile_start(t), nv = tile_valid(t);
-    const bf16_t* base = a.qkv + (int64_t)kr0 * ld + D + h * HD;
-    if (nv == KTILE) {
+    const int kr0 = tile_start(t);
+    const int ext = min(a.rows - kr0, KTILE) * (int)ld * 2 - (int)head_off * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)i * 16 * ld + koff0),
-                                         LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
-    } else {  // last tile of a range: keys past its end are clamped
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)min(16 * i + kk0, nv - 1) * ld + hc * 8),
-                                         LDS_PTR(kb + (i * 4 + wave) * 512), 16, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i) buffer_load_lds16(a.qkv + (int64_t)kr0 * ld + head_off, ext, kb + (i * 4 + wave) * 512, koff[i], 0);
   };
+  // V^T tiles through a buffer resource over this head's 128 rows of vT
+  // (columns up to S_pad), with the tile's first column in the scalar offset
+  const bf16_t* vbase = a.vT + (int64_t)(h * HD) * a.S_pad;
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (voff0 + (uint32_t)(i * 32 * a.S_pad)) * 2;
   auto dma_v = [&](int t, bf16_t* vb) {
-    const bf16_t* base = a.vT + (int64_t)(h * HD) * a.S_pad + tile_start(t);
+    const int c0 = tile_start(t) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)i * 32 * a.S_pad + voff0),
-                                       LDS_PTR(vb + (i * 4 + wave) * 512), 16, 0, 0);
+      buffer_load_lds16(vbase, HD * a.S_pad * 2, vb + (i * 4 + wave) * 512, voff[i], c0);
   };
   // S^T for 64 keys x this wave's 32 queries; with MASK, keys past nv -> -inf
   // Operand reads run AHEAD reads ahead of the MFMA that consumes them

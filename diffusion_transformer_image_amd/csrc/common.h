@@ -81,6 +81,19 @@ ZI_DEV void dma_barrier() {
   __syncthreads();
 }
 
+// One 16-byte-per-lane direct-to-LDS load through a raw buffer resource
+// (base, extent in bytes; the per-lane offset in a register, a uniform offset
+// in a scalar): lanes whose byte offset reaches past the extent read zeros.
+// The buffer form is counted on the vector-memory counter only; the flat
+// (global_load_lds) form is taken by the compiler as a possible LDS access
+// of unknown order, after which it can only wait for all LDS reads at once.
+// Lanes write LDS at lds + 16 * lane (the wave-uniform base goes to M0).
+ZI_DEV void buffer_load_lds16(const void* base, int extent, void* lds, uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, extent,
+                                                                     0x00020000);  // raw dword access
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // v from lane (lane ^ M) of the same 16-lane row, by DPP moves: quad
 // permutations for 1 and 2 (and 3), a half-row mirror (lane ^ 7) after a
 // quad xor 3 for 4, a row rotation by 8 for 8 (every source lane is inside

@@ -602,6 +602,9 @@ int zimg_dit::allocate() {
   cap_rows_max = (int64_t)c.max_batch * round_up(c.max_caption_tokens, row_align);
   S_max = img_rows_max + cap_rows_max;
   S_pad = round_up(S_max, 64) + 64;
+  // the attention reads a head's 128 rows of v^T through one 32-bit buffer extent
+  if (S_pad > (1 << 22))
+    return set_err(ZIMG_EINVAL, "max_batch x (image + caption rows) = %lld rows exceeds 2^22", (long long)S_max);
   ALLOC(x, S_max * D);
   ALLOC(h, S_max * D);
   ALLOC(qkv, S_max * 3 * D);
@@ -936,6 +939,7 @@ int zimg_dit::run_block(int bi, const Layout& L, bool h_ready, int next, hipStre
                     n_items_stage[stage],
                     H,
                     (int)S_pad,
+                    (int)S_max,
                     (float)(1.4426950408889634 / std::sqrt(128.0)),
                     attn_full[stage],
                     attn_split[stage],
@@ -1200,6 +1204,7 @@ namespace {
 // seg [B][4] = (r0 of the first range, its rows, r0 of the second, its rows).
 struct AttnOpPlan {
   int n_items = 0, n_full = 0, split = 1;
+  int rows = 0;           // rows of qkv the segments reach (the key rows' bound)
   size_t header = 0;      // bytes of the work list at the start of the workspace
   size_t part_bytes = 0;  // bytes of split partials the plan uses
   zimg::AttnPlanArgs pa{};
@@ -1209,7 +1214,7 @@ int attention_op_plan(int32_t H, int32_t B, const int32_t* seg, int64_t S_pad, s
   if (H < 1 || H > 256) return set_err(ZIMG_EINVAL, "attention: H %d outside 1..256", H);
   if (B < 1 || B > zimg::ATTN_OP_MAX_B) return set_err(ZIMG_EINVAL, "attention: B %d outside 1..%d", B, zimg::ATTN_OP_MAX_B);
   if (!seg) return set_err(ZIMG_EINVAL, "attention: segments array is NULL");
-  if (S_pad < 64 || S_pad % 8 || S_pad > (1 << 24)) return set_err(ZIMG_EINVAL, "attention: S_pad %lld must be a multiple of 8 in 64..2^24", (long long)S_pad);
+  if (S_pad < 64 || S_pad % 8 || S_pad > (1 << 22)) return set_err(ZIMG_EINVAL, "attention: S_pad %lld must be a multiple of 8 in 64..2^22", (long long)S_pad);
   P.pa.B = B;
   int n = 0;
   for (int b = 0; b < B; ++b) {
@@ -1222,6 +1227,7 @@ int attention_op_plan(int32_t H, int32_t B, const int32_t* seg, int64_t S_pad, s
         return set_err(ZIMG_EINVAL, "attention: sample %d range %d: rows %lld..%lld (rounded up to 64 keys) exceed S_pad %lld", b, r, (long long)r0, (long long)(r0 + len), (long long)S_pad);
       q.r0[r] = (int)r0;
       q.n[r] = (int)len;
+      if (len > 0) P.rows = std::max(P.rows, (int)(r0 + len));
     }
     P.pa.item_off[b] = n;
     n += (q.n[0] + 127) / 128 + (q.n[1] + 127) / 128;
@@ -1280,6 +1286,7 @@ int attention_op(const void* qkv, const void* vT, int64_t S_pad, void* out, int3
                     P.n_items,
                     H,
                     (int)S_pad,
+                    P.rows,
                     (float)(1.4426950408889634 / std::sqrt(128.0)),
                     P.n_full,
                     P.split,

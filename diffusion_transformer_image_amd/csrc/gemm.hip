@@ -13,7 +13,7 @@
 //
 // Workgroup tile BM x BN, K-step 64, 512 threads = 8 waves (2 waves per
 // SIMD, so one wave's MFMAs cover the other's memory waits).  Operands go
-// global -> LDS directly (global_load_lds_dwordx4, no register staging),
+// global -> LDS directly (buffer_load_dwordx4 ... lds, no register staging),
 // A into two stage buffers and W into three: early in each K-step the next
 // stage of A and the stage after next of W are issued, and one barrier per
 // K-step publishes a stage, waiting for all but the newest W loads.  LDS
@@ -402,17 +402,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
     const int p = (i * NW + wid) * 64 + lane, row = p >> 3, lc = (p & 7) ^ ((row >> 1) & 7);
     b_off[i] = (uint32_t)((min(n0 + row, N - 1) - n0) * ldw * 2 + lc * 16);
   }
+  // The loads read through buffer resources over the tile's rows of A and
+  // W (their extent); a K-step's offset is the uniform scalar offset.
+  const int a_ext = (int)(min(BM, M - m0) * lda * 2), b_ext = (int)(min(BN, N - n0) * ldw * 2);
   auto issue_a = [&](int kt, bf16_t* as) {
-    const char* ak = a_base + (int64_t)kt * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < NA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(ak + a_off[i]), LDS_PTR(as + (i * NW + wid) * 512), 16, 0, 0);
+    for (int i = 0; i < NA; ++i) buffer_load_lds16(a_base, a_ext, as + (i * NW + wid) * 512, a_off[i], kt * (BK * 2));
   };
   auto issue_b = [&](int kt, bf16_t* bs) {
-    const char* bk = b_base + (int64_t)kt * (BK * 2);
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bk + b_off[i]), LDS_PTR(bs + (i * NW + wid) * 512), 16, 0, 0);
+    for (int i = 0; i < NB; ++i) buffer_load_lds16(b_base, b_ext, bs + (i * NW + wid) * 512, b_off[i], kt * (BK * 2));
   };
 
   using AccT = typename AccOf<I8>::T;
@@ -798,6 +797,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   constexpr int LDS_BYTES = (2 * BM + 3 * BN) * BK * 2;
   constexpr int U = I8 ? 2 : 1;  // elements per bf16-sized unit
   const int K = g.K / U;
+  // a tile's rows of A and W are read through 32-bit buffer extents
+  if ((int64_t)BM * (g.lda / U) * 2 > INT32_MAX || (int64_t)BN * (g.ldw / U) * 2 > INT32_MAX) return hipErrorInvalidValue;
   GemmSplit sp = g.split;
   sp.n_cu *= (160 * 1024) / LDS_BYTES;  // workgroups resident at once
   const int gm = group_rows(ROLE, tiles_n);

@@ -157,6 +157,7 @@ struct AttnArgs {
   const AttnItem* items;
   const AttnSeg* segs;
   int n_items, H, S_pad;
+  int rows;  // rows of qkv (key rows at or past it are never read)
   float scale_log2;
   int n_full;   // pairs computed whole (== n_items * H when nothing is split)
   int split;    // chunks per remaining pair (1: none)

@@ -179,7 +179,7 @@ int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stat
  *         (the v part is not read), q and k already QK-normalised and rotated;
  *         16-byte aligned
  *   vT    DEVICE bf16 [H 128][S_pad]: v transposed (element [h 128 + d][r]),
- *         16-byte aligned; S_pad a multiple of 8, 64..2^24
+ *         16-byte aligned; S_pad a multiple of 8, 64..2^22
  *   out   DEVICE bf16 [rows, H 128], 8-byte aligned; only the rows of the
  *         segments are written
  *   seg   HOST int32 [B][4]: (start, rows) of the first range, (start, rows)

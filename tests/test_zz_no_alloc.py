@@ -57,12 +57,12 @@ def test_noalloc_matches_workspace_entry_point_twice():
 
 
 def test_noalloc_rejects_a_work_list_beyond_the_scratch():
-    """64 samples of two 2^24-row ranges need a 268 MB work list, more than
+    """64 samples of two 2^22-row ranges need a 67 MB work list, more than
     the 40 MiB scratch: refused with an error that names the limit, before
     anything is enqueued (the buffers are allocated but never read)."""
     torch = _torch()
     from diffusion_transformer_image_amd import binding
-    H, S_pad = 1, 1 << 24
+    H, S_pad = 1, 1 << 22
     qkv = torch.empty((S_pad, 3 * 128), dtype=torch.bfloat16, device="cuda")
     vT = torch.empty((128, S_pad), dtype=torch.bfloat16, device="cuda")
     out = torch.empty((S_pad, 128), dtype=torch.bfloat16, device="cuda")
