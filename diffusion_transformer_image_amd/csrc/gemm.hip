@@ -201,9 +201,14 @@ ZI_DEV void qk_weights(const EpiArgs& ep, int sec, int k, float (&wv)[8]) {
 //    and store the head back in place;
 //  - v: 16-byte runs of 8 rows of one column are stored into the transposed
 //    copy vT[head*128 + d][row].
-// Staging layouts keep LDS accesses free of bank conflicts: q/k rows of
-// 512 B hold their 16-byte chunk c at position c ^ (r & 15); v columns of
-// 512 B (256 rows) hold chunk k (rows 8k..8k+7) at position k ^ (col & 15).
+// Staging layouts keep LDS accesses free of bank conflicts.  q/k rows of
+// 512 B hold their 16-byte chunk c at position c ^ qk_swz(r); the
+// accumulator-order writes go out as 4-byte pairs of adjacent columns (the
+// two lanes of a column pair swap one of their two rows), and one such store
+// covers rows r, r + 1, r + 4, r + 5, which qk_swz places in the four
+// different 64-byte bank groups.  v columns of 512 B (256 rows) hold chunk k
+// (rows 8k..8k+7) at position k ^ (col & 15).
+ZI_DEV int qk_swz(int r) { return ((r & 1) << 2) | (((r >> 2) & 1) << 3); }
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0,
                                                   int M, const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2,
@@ -217,16 +222,23 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
   auto region = [&](int k) { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
   __syncthreads();  // every wave has finished reading the operand buffers
   if (sec < 2) {
+    // a lane holds rows r, r + 1 of its column; it stores row r + odd of the
+    // column pair (col & ~1, col | 1), taking the other column from lane ^ 1
+    const int odd = lrow & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // [other.hi | own.hi] : [own.lo | other.lo]
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       bf16_t* rg = region(wm * 2 + (i >> 1));
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int col = wn * 64 + j * 32 + lrow;
+        const int cc = wn * 64 + j * 32 + (lrow & ~1);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          rg[(r & 63) * 256 + (((col >> 3) ^ (r & 15)) << 3) + (col & 7)] = f2bf(acc[i][j][e]);
+        for (int e = 0; e < 16; e += 2) {
+          const uint32_t own = pack2bf(acc[i][j][e], acc[i][j][e + 1]);
+          const uint32_t other = __float_as_uint(lane_xor<1>(__uint_as_float(own)));
+          const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3) + odd;
+          *reinterpret_cast<uint32_t*>(rg + (r & 63) * 256 + (((cc >> 3) ^ qk_swz(r)) << 3) + (cc & 7)) =
+              __builtin_amdgcn_perm(other, own, sel);
         }
       }
     }
@@ -241,7 +253,7 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
     for (int p = 0; p < 16; ++p) {
       const int u = p * 32 + wid * 4 + (lane >> 4);  // (row, head) unit
       const int r = u >> 1, hl = u & 1;               // r >> 6 == p >> 2
-      const u32x4 x = *reinterpret_cast<const u32x4*>(region(p >> 2) + (r & 63) * 256 + (((hl * 16 + k) ^ (r & 15)) << 3));
+      const u32x4 x = *reinterpret_cast<const u32x4*>(region(p >> 2) + (r & 63) * 256 + (((hl * 16 + k) ^ qk_swz(r)) << 3));
       const int row = m0 + r;
       const int64_t trow = (int64_t)ep.trow0 + min(row, M - 1);
       qk_rope_unit(x, k, wv, ep.eps, ep.cos_t + trow * 64, ep.sin_t + trow * 64,
