@@ -157,17 +157,21 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // Operand reads run AHEAD reads ahead of the MFMA that consumes them
   // (a small ring of fragments), so an MFMA never waits on the LDS read issued
   // just before it.
-  auto qk = [&](const bf16_t* kb, f32x16* st) {
-    st[0] = f32x16{};
-    st[1] = f32x16{};
+  // S^T score MFMAs [i0, i1) of a tile (16 in all) with their K fragment
+  // reads AHEAD ahead, in a ring shared by the two calls that make one tile
+  bf16x8 kf[AHEAD + 1];
+  auto qk = [&](const bf16_t* kb, f32x16* st, int i0, int i1) {
     auto kread = [&](int i) {  // i = 2 ks + tt
       return *reinterpret_cast<const bf16x8*>(kb + ((i & 1) * 32 + lrow) * HD + (((2 * (i >> 1) + lhalf) ^ swk) << 3));
     };
-    bf16x8 kf[AHEAD + 1];
+    if (i0 == 0) {
+      st[0] = f32x16{};
+      st[1] = f32x16{};
 #pragma unroll
-    for (int i = 0; i < AHEAD; ++i) kf[i] = kread(i);
+      for (int i = 0; i < AHEAD; ++i) kf[i] = kread(i);
+    }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = i0; i < i1; ++i) {
       if (i + AHEAD < 16) kf[(i + AHEAD) % (AHEAD + 1)] = kread(i + AHEAD);
       st[i & 1] = mfma32(kf[i % (AHEAD + 1)], qf[i >> 1], st[i & 1]);
     }
@@ -201,14 +205,16 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // max), so a weight 2^(s - m) rounds to bf16 the same way whatever m is:
   // a pair split into key chunks (each with its own m) weighs every key as
   // the whole pair would, and the merge scales chunks by exact powers of two.
-  auto stats = [&](f32x16* st) {
+  auto stats_max = [&](f32x16* st) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, st[tt][e]);
     mx = pair_max(mx) * sl2;
-    const float mnew = mx > m + RESCALE_SLACK ? ceilf(mx) : m;
+    return mx > m + RESCALE_SLACK ? ceilf(mx) : m;
+  };
+  auto stats_apply = [&](float mnew) {
     if (__any(mnew != m)) {
       const float alpha = __builtin_amdgcn_exp2f(m - mnew);
 #pragma unroll
@@ -251,15 +257,30 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
       o[i & 3] = mfma32(vf[i % (AHEAD + 1)], pf, o[i & 3]);
     }
   };
-  // the issue order of one pipelined half: scores of the next tile interleaved
-  // with the exponentials of the current one, then the PV product
-  auto pin_order = [&]() {
+  // the issue order of the rest of a pipelined half: the remaining scores of
+  // the next tile interleaved with the exponentials of the current one, then
+  // the PV product
+  // The first NPRE score MFMAs of the next tile are issued before the row
+  // maxima of the current one, so that dependent chain (16 three-way maxima,
+  // the lane-pair exchange, the ceiling) runs while they execute: -1.7 % per
+  // launch against starting the scores after it.
+  constexpr int NPRE = 4;
+  constexpr int EXPV = (64 + (16 - NPRE) - 1) / (16 - NPRE);  // exponential-phase VALU per score MFMA
+  auto pin_pre = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first K operand reads
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < NPRE; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (row-max chain)
+    }
+  };
+  auto pin_order = [&]() {
+#pragma unroll
+    for (int g = NPRE; g < 16; ++g) {
       if (g + AHEAD < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (K operand)
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores)
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (exponentials)
+      __builtin_amdgcn_sched_group_barrier(0x002, EXPV, 0);  // VALU (exponentials)
     }
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first V operand reads
 #pragma unroll
@@ -273,12 +294,15 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // Pipeline: in the half that handles tile t, the scores of tile t+1 are
   // computed while tile t is exponentiated and multiplied into O.  K(t+2) and
   // V(t+1) are loaded meanwhile into the buffers freed by the previous half.
-  // Masking (partial tiles only) and the rescale are wave-uniform branches
-  // before the pinned matrix/vector interleave.
+  // Masking (partial tiles only) and the rescale are wave-uniform branches;
+  // the first score MFMAs of tile t+1 are issued before the rescale's test.
   auto half = [&](const bf16_t* kn, const bf16_t* vc, f32x16* scur, f32x16* snext, int nv_cur) {
     if (nv_cur < KTILE) mask(scur, nv_cur);
-    stats(scur);
-    qk(kn, snext);
+    qk(kn, snext, 0, NPRE);
+    const float mnew = stats_max(scur);
+    pin_pre();
+    stats_apply(mnew);
+    qk(kn, snext, NPRE, 16);
     expsum(scur);
     pv(vc, scur);
     pin_order();
@@ -333,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   dma_k(clamp_t(2), K2);
   load_barrier();  // K(0), V(0), K(1)
   f32x16 sc[2], sn[2];
-  qk(K0, sc);
+  qk(K0, sc, 0, 16);
   // pairs cycle through the three K-buffer assignments (j = 0, 2, 4 mod 6)
   int j = 0;
   for (; j + 6 <= Tp; j += 6) {
