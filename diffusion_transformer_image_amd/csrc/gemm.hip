@@ -202,13 +202,13 @@ ZI_DEV void qk_weights(const EpiArgs& ep, int sec, int k, float (&wv)[8]) {
 //  - v: 16-byte runs of 8 rows of one column are stored into the transposed
 //    copy vT[head*128 + d][row].
 // Staging layouts keep LDS accesses free of bank conflicts.  q/k rows of
-// 512 B hold their 16-byte chunk c at position c ^ qk_swz(r); the
+// 512 B hold their 16-byte chunk c at position c ^ stage_swz(r); the
 // accumulator-order writes go out as 4-byte pairs of adjacent columns (the
 // two lanes of a column pair swap one of their two rows), and one such store
 // covers rows r, r + 1, r + 4, r + 5, which qk_swz places in the four
 // different 64-byte bank groups.  v columns of 512 B (256 rows) hold chunk k
 // (rows 8k..8k+7) at position k ^ (col & 15).
-ZI_DEV int qk_swz(int r) { return ((r & 1) << 2) | (((r >> 2) & 1) << 3); }
+ZI_DEV int stage_swz(int r) { return ((r & 1) << 2) | (((r >> 2) & 1) << 3); }
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0,
                                                   int M, const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2,
@@ -237,7 +237,7 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
           const uint32_t own = pack2bf(acc[i][j][e], acc[i][j][e + 1]);
           const uint32_t other = __float_as_uint(lane_xor<1>(__uint_as_float(own)));
           const int r = wm * 128 + i * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3) + odd;
-          *reinterpret_cast<uint32_t*>(rg + (r & 63) * 256 + (((cc >> 3) ^ qk_swz(r)) << 3) + (cc & 7)) =
+          *reinterpret_cast<uint32_t*>(rg + (r & 63) * 256 + (((cc >> 3) ^ stage_swz(r)) << 3) + (cc & 7)) =
               __builtin_amdgcn_perm(other, own, sel);
         }
       }
@@ -253,7 +253,7 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
     for (int p = 0; p < 16; ++p) {
       const int u = p * 32 + wid * 4 + (lane >> 4);  // (row, head) unit
       const int r = u >> 1, hl = u & 1;               // r >> 6 == p >> 2
-      const u32x4 x = *reinterpret_cast<const u32x4*>(region(p >> 2) + (r & 63) * 256 + (((hl * 16 + k) ^ qk_swz(r)) << 3));
+      const u32x4 x = *reinterpret_cast<const u32x4*>(region(p >> 2) + (r & 63) * 256 + (((hl * 16 + k) ^ stage_swz(r)) << 3));
       const int row = m0 + r;
       const int64_t trow = (int64_t)ep.trow0 + min(row, M - 1);
       qk_rope_unit(x, k, wv, ep.eps, ep.cos_t + trow * 64, ep.sin_t + trow * 64,
@@ -291,8 +291,9 @@ __device__ __forceinline__ void qkv_rope_epilogue(const f32x16 (&acc)[BM / WM / 
 // 256x128 output) go through LDS so that global stores are 16-byte runs of
 // whole rows instead of 2-byte stores from the accumulator layout.  The four
 // 32 KB operand buffers hold the output tile, row r in buffer r / RPB; the
-// 16-byte chunk k of a row is stored at position k ^ (r & 15), so neither
-// the accumulator-order writes nor the row-order reads conflict.
+// 16-byte chunk k of a row is stored at position k ^ stage_swz(r), and the
+// accumulator-order writes go out as 4-byte pairs of adjacent columns, as in
+// the QKV epilogue, so neither they nor the row-order reads conflict.
 template <int BM, int BN, int WM, int WN, int EPI>
 __device__ __forceinline__ void staged_bf16_epilogue(const f32x16 (&acc)[BM / WM / 32][BN / WN / 32], int m0, int n0,
                                                      int M, const EpiArgs& ep, bf16_t* s0, bf16_t* s1, bf16_t* s2,
@@ -308,19 +309,27 @@ __device__ __forceinline__ void staged_bf16_epilogue(const f32x16 (&acc)[BM / WM
   const int lrow = lane & 31, lhalf = lane >> 5;
   auto region = [&](int k) { return k == 0 ? s0 : k == 1 ? s1 : k == 2 ? s2 : s3; };
   __syncthreads();  // every wave has finished reading the operand buffers
+  const int odd = lrow & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // [other.hi | own.hi] : [own.lo | other.lo]
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int rb = wm * 128 + i * 32;  // 32 rows, all in one buffer
     bf16_t* rg = region(rb / RPB);
 #pragma unroll
     for (int j = 0; j < TN; j += (EPI == EPI_SWIGLU ? 2 : 1)) {
-      const int c = EPI == EPI_SWIGLU ? wn * 32 + lrow : wn * 64 + j * 32 + lrow;
+      const int cc = (EPI == EPI_SWIGLU ? wn * 32 : wn * 64 + j * 32) + (lrow & ~1);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = rb + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-        float v = acc[i][j][e];
-        if constexpr (EPI == EPI_SWIGLU) v = silu(v) * acc[i][j + 1][e];
-        rg[(r % RPB) * OW + (((c >> 3) ^ (r & 15)) << 3) + (c & 7)] = f2bf(v);
+      for (int e = 0; e < 16; e += 2) {
+        float v0 = acc[i][j][e], v1 = acc[i][j][e + 1];
+        if constexpr (EPI == EPI_SWIGLU) {
+          v0 = silu(v0) * acc[i][j + 1][e];
+          v1 = silu(v1) * acc[i][j + 1][e + 1];
+        }
+        const uint32_t own = pack2bf(v0, v1);
+        const uint32_t other = __float_as_uint(lane_xor<1>(__uint_as_float(own)));
+        const int r = rb + (e >> 2) * 8 + lhalf * 4 + (e & 3) + odd;
+        *reinterpret_cast<uint32_t*>(rg + (r % RPB) * OW + (((cc >> 3) ^ stage_swz(r)) << 3) + (cc & 7)) =
+            __builtin_amdgcn_perm(other, own, sel);
       }
     }
   }
@@ -331,7 +340,7 @@ __device__ __forceinline__ void staged_bf16_epilogue(const f32x16 (&acc)[BM / WM
   for (int it = 0; it < BM * CPR / 512; ++it) {
     const int q = it * 512 + tid, r = q / CPR, k = q % CPR;
     if (m0 + r >= M) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(region(r / RPB) + (r % RPB) * OW + ((k ^ (r & 15)) << 3));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region(r / RPB) + (r % RPB) * OW + ((k ^ stage_swz(r)) << 3));
     *reinterpret_cast<u32x4*>(C + (int64_t)(m0 + r) * ep.ldc + c0 + k * 8) = v;
   }
 }
