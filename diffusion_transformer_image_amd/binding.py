@@ -21,6 +21,7 @@ ZIMG_EUNSUPPORTED = -3
 ZIMG_ENOMEM = -4
 ZIMG_EHIP = -5
 ZIMG_ESTATE = -6
+ZIMG_ENONFINITE = -7
 ZIMG_F32 = 0
 ZIMG_BF16 = 1
 EPI_BF16 = 0
@@ -28,7 +29,8 @@ EPI_F32_BIAS = 1
 EPI_SWIGLU = 2
 
 _CODES = {ZIMG_EINVAL: "EINVAL", ZIMG_EWEIGHT: "EWEIGHT", ZIMG_EUNSUPPORTED: "EUNSUPPORTED",
-          ZIMG_ENOMEM: "ENOMEM", ZIMG_EHIP: "EHIP", ZIMG_ESTATE: "ESTATE"}
+          ZIMG_ENOMEM: "ENOMEM", ZIMG_EHIP: "EHIP", ZIMG_ESTATE: "ESTATE",
+          ZIMG_ENONFINITE: "ENONFINITE"}
 
 
 class ZimgError(RuntimeError):
@@ -48,6 +50,7 @@ class Config(ctypes.Structure):
         ("final_eps", ctypes.c_float), ("max_batch", ctypes.c_int32),
         ("max_image_tokens", ctypes.c_int32), ("max_caption_tokens", ctypes.c_int32),
         ("batch_invariant", ctypes.c_int32), ("linear_int8", ctypes.c_int32), ("token_pad", ctypes.c_int32),
+        ("check_finite", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -147,11 +147,26 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (voff0 + (uint32_t)(i * 32 * a.S_pad)) * 2;
+  // Keys past the end of a range get weight exactly 0, but 0 * v is NaN
+  // where v is not finite, and a partial tile's last key columns hold the
+  // rows after the range: another sample's tokens, or rows of no segment.
+  // So in a partial tile the 8-key chunks that lie wholly past the range's
+  // end are loaded from past the buffer extent, which fills them with zeros;
+  // the keys after the end inside the last chunk are the range's own
+  // alignment rows (ranges start at multiples of 8), which are kept finite.
+  const int vkc = (lane & 7) ^ ((dd0 >> 1) & 7);  // the 8-key chunk this lane's V^T loads hold
+  const int vext = HD * a.S_pad * 2;
   auto dma_v = [&](int t, bf16_t* vb) {
-    const int c0 = tile_start(t) * 2;
+    const int c0 = tile_start(t) * 2, nv = tile_valid(t);
+    if (nv == KTILE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      buffer_load_lds16(vbase, HD * a.S_pad * 2, vb + (i * 4 + wave) * 512, voff[i], c0);
+      for (int i = 0; i < 4; ++i) buffer_load_lds16(vbase, vext, vb + (i * 4 + wave) * 512, voff[i], c0);
+    } else {
+      const bool past = vkc * 8 >= nv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        buffer_load_lds16(vbase, vext, vb + (i * 4 + wave) * 512, past ? (uint32_t)vext : voff[i], c0);
+    }
   };
   // S^T for 64 keys x this wave's 32 queries; with MASK, keys past nv -> -inf
   // Operand reads run AHEAD reads ahead of the MFMA that consumes them

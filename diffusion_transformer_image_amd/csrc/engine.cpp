@@ -17,6 +17,7 @@
 // blocks on image tokens, 2 context-refiner blocks on text tokens).
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -166,7 +167,7 @@ std::vector<ManifestEntry> build_manifest(const zimg_dit_config& c) {
 // manifest query while another thread creates an engine), hence the lock.
 // Entries are never removed, so a returned reference stays valid unlocked.
 // (the key is the config's bytes: 25 four-byte fields, no padding)
-static_assert(sizeof(zimg_dit_config) == 25 * 4, "zimg_dit_config must have no padding");
+static_assert(sizeof(zimg_dit_config) == 26 * 4, "zimg_dit_config must have no padding");
 const std::vector<ManifestEntry>& cached_manifest(const zimg_dit_config& c) {
   static std::mutex mu;
   static std::map<std::string, std::unique_ptr<std::vector<ManifestEntry>>> cache;
@@ -212,6 +213,7 @@ int check_config(const zimg_dit_config* c) {
   if (c->batch_invariant != 0 && c->batch_invariant != 1) return set_err(ZIMG_EINVAL, "batch_invariant must be 0 or 1");
   if (c->linear_int8 != 0 && c->linear_int8 != 1) return set_err(ZIMG_EINVAL, "linear_int8 must be 0 or 1");
   if (c->token_pad != 0 && c->token_pad != 32) return set_err(ZIMG_EUNSUPPORTED, "token_pad must be 0 or 32");
+  if (c->check_finite != 0 && c->check_finite != 1) return set_err(ZIMG_EINVAL, "check_finite must be 0 or 1");
   return ZIMG_OK;
 }
 
@@ -386,6 +388,13 @@ struct zimg_dit {
     int attn_split[3] = {1, 1, 1};
   } geo[kGeoSlots];
   uint64_t geo_clock = 0;
+  // geometry of the previous call; when it changes, rows that were real
+  // tokens may become alignment rows, which must not keep stale values
+  std::vector<int32_t> last_key;
+  // check_finite: the lowest stage tag whose rows held a non-finite value
+  // (INT_MAX: none), and its pinned host copy
+  int* finite_flag = nullptr;
+  int* finite_host = nullptr;
   size_t staging_bytes = 0;
   int64_t max_items = 0;
   // views of the slot of the current geometry
@@ -477,6 +486,7 @@ struct zimg_dit {
   }
 
   ~zimg_dit() {
+    if (finite_host) (void)hipHostFree(finite_host);
     for (hipEvent_t e : prof.ev) (void)hipEventDestroy(e);
     for (void* p : allocations) (void)hipFree(p);
     for (GeoSlot& g : geo) {
@@ -606,6 +616,14 @@ int zimg_dit::allocate() {
   if (S_pad > (1 << 22))
     return set_err(ZIMG_EINVAL, "max_batch x (image + caption rows) = %lld rows exceeds 2^22", (long long)S_max);
   ALLOC(x, S_max * D);
+  if (c.check_finite) {
+    ALLOC(finite_flag, 1);
+    hipError_t e = hipHostMalloc((void**)&finite_host, sizeof(int), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      finite_host = nullptr;
+      return set_err(ZIMG_ENOMEM, "hipHostMalloc(4) failed: %s", hipGetErrorString(e));
+    }
+  }
   ALLOC(h, S_max * D);
   ALLOC(qkv, S_max * 3 * D);
   ALLOC(vT, (int64_t)c.n_heads * 128 * S_pad);
@@ -837,6 +855,18 @@ int zimg_dit::prepare(const Layout& L, const float* t, hipStream_t s) {
     HIP_TRY(hipMemcpyAsync(G.items, itm, 3 * max_items * sizeof(zimg::AttnItem), hipMemcpyHostToDevice, s));
     HIP_TRY(hipEventRecord(G.done, s));
     G.key = key;
+  }
+  if (key != last_key) {
+    // Alignment rows (in no attention segment) are computed like tokens from
+    // rows of xin, capn and o that no call writes, so they stay finite as
+    // long as those rows start finite; after a change of geometry they may
+    // hold an earlier call's tokens, which are cleared here.  Attention reads
+    // the alignment rows just past a range's end as keys of weight 0, and
+    // 0 * v must not become NaN.
+    HIP_TRY(zimg::launch_fill(reinterpret_cast<float*>(xin), 0.0f, img_rows_max * (c.patch * c.patch * c.in_channels) / 2, s));
+    HIP_TRY(zimg::launch_fill(reinterpret_cast<float*>(capn), 0.0f, cap_rows_max * c.cap_feat_dim / 2, s));
+    HIP_TRY(zimg::launch_fill(reinterpret_cast<float*>(o), 0.0f, S_max * c.hidden / 2, s));
+    last_key = key;
   }
   {
     GeoSlot& G = geo[slot];
@@ -1072,6 +1102,21 @@ int zimg_dit::forward(const float* const* latents, const Layout& L, const void* 
   }
   rc = prof_stop(s);
   if (rc) return rc;
+  // check_finite: every stage's sequence rows (each sample's image and
+  // caption runs; alignment rows are never read) are scanned after it runs
+  auto scan_rows = [&](int tag) -> hipError_t {
+    for (int b = 0; b < L.B; ++b) {
+      hipError_t e = zimg::launch_scan_finite(x + (int64_t)L.img_off[b] * D, (int64_t)L.Nseq[b] * D, tag, finite_flag, s);
+      if (e == hipSuccess)
+        e = zimg::launch_scan_finite(x + (int64_t)L.cap_off[b] * D, (int64_t)L.Lseq[b] * D, tag, finite_flag, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  if (c.check_finite) {
+    HIP_TRY(zimg::launch_set_int(finite_flag, INT_MAX, s));
+    HIP_TRY(scan_rows(0));
+  }
   const size_t slot_bytes = (size_t)L.S * D * 4;
   if (cap_buf) HIP_TRY(hipMemcpyAsync(cap_buf, x, slot_bytes, hipMemcpyDeviceToDevice, s));
 
@@ -1088,6 +1133,7 @@ int zimg_dit::forward(const float* const* latents, const Layout& L, const void* 
     final_ready = next == 2;
     if (cap_buf) HIP_TRY(hipMemcpyAsync((char*)cap_buf + (size_t)(bi + 1) * slot_bytes, x, slot_bytes,
                                         hipMemcpyDeviceToDevice, s));
+    if (c.check_finite) HIP_TRY(scan_rows(bi + 1));
   }
   rc = prof_start(K_FINAL, s);
   if (rc) return rc;
@@ -1125,7 +1171,22 @@ int zimg_dit::forward(const float* const* latents, const Layout& L, const void* 
   } else {
     for (int b = 0; b < L.B; ++b) HIP_TRY(final_gemm(L.img_off[b], L.Npad[b], b, outs[b]));
   }
-  return prof_stop(s);
+  rc = prof_stop(s);
+  if (rc || !c.check_finite) return rc;
+  // check_finite: scan the outputs, then wait for the verdict
+  const int nb_all = (int)blocks.size();
+  for (int b = 0; b < L.B; ++b)
+    HIP_TRY(zimg::launch_scan_finite(outs[b], (int64_t)c.in_channels * L.Hp[b] * c.patch * L.Wp[b] * c.patch, nb_all + 1,
+                                     finite_flag, s));
+  HIP_TRY(hipMemcpyAsync(finite_host, finite_flag, sizeof(int), hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  const int bad = *finite_host;
+  if (bad == INT_MAX) return ZIMG_OK;
+  if (bad == 0) return set_err(ZIMG_ENONFINITE, "non-finite values in the sequence after the embeddings");
+  if (bad <= nb_all)
+    return set_err(ZIMG_ENONFINITE, "non-finite values in the sequence after block %d (%s)", bad - 1,
+                   blocks[bad - 1].prefix.c_str());
+  return set_err(ZIMG_ENONFINITE, "non-finite values in the model output");
 }
 
 int zimg_dit::run_blocks(float* x_io, const Layout& L, const float* t, int first, int n, hipStream_t s) {

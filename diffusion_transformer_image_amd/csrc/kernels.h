@@ -209,5 +209,9 @@ hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g,
 hipError_t launch_fill(float* p, float v, int64_t n, hipStream_t s);
 // rows [r0, r0 + n) of x (row length and stride D) = v[0 .. D)
 hipError_t launch_set_rows(float* x, int D, const float* v, int r0, int n, hipStream_t s);
+// non-finite scan: *first_bad = min(*first_bad, tag) if x[0, n) holds a NaN or
+// an infinity; set_int writes one int
+hipError_t launch_scan_finite(const float* x, int64_t n, int tag, int* first_bad, hipStream_t s);
+hipError_t launch_set_int(int* p, int v, hipStream_t s);
 
 }  // namespace zimg

@@ -9,6 +9,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace zimg {
 namespace {
 
@@ -106,6 +108,17 @@ __global__ __launch_bounds__(256) void set_rows_kernel(float* x, int D, const fl
   for (int d = threadIdx.x; d < D; d += 256) row[d] = v[d];
 }
 
+// *first_bad = min(*first_bad, tag) when x[0, n) holds a NaN or an infinity
+__global__ __launch_bounds__(256) void scan_finite_kernel(const float* __restrict__ x, int64_t n, int tag,
+                                                          int* first_bad) {
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    bad |= !__builtin_isfinite(x[i]);
+  if (bad) atomicMin(first_bad, tag);
+}
+
+__global__ void set_int_kernel(int* p, int v) { *p = v; }
+
 __global__ void fill_kernel(float* p, float v, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -153,6 +166,18 @@ hipError_t launch_cfg_euler(float* x, const float* oc, const float* ou, float g,
 hipError_t launch_set_rows(float* x, int D, const float* v, int r0, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(set_rows_kernel, dim3(n), dim3(256), 0, s, x + (int64_t)r0 * D, D, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_finite(const float* x, int64_t n, int tag, int* first_bad, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(scan_finite_kernel, dim3(grid), dim3(256), 0, s, x, n, tag, first_bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_int(int* p, int v, hipStream_t s) {
+  hipLaunchKernelGGL(set_int_kernel, dim3(1), dim3(1), 0, s, p, v);
   return hipGetLastError();
 }
 

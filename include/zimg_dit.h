@@ -44,6 +44,8 @@ extern "C" {
 #define ZIMG_ENOMEM (-4)       /* device or host allocation failed */
 #define ZIMG_EHIP (-5)         /* HIP runtime error (message carries hipGetErrorString) */
 #define ZIMG_ESTATE (-6)       /* call out of order (e.g. forward before all weights set) */
+#define ZIMG_ENONFINITE (-7)   /* check_finite: a NaN or infinity appeared (the message names
+                                  the first stage: embeddings, block, or output) */
 
 /* ---- element types ----------------------------------------------------- */
 #define ZIMG_F32 0
@@ -109,6 +111,13 @@ typedef struct zimg_dit_config {
                                 stream needs a key mask).  The row layout is then the
                                 one of the padded counts (zimg_row_layout with each
                                 count rounded up to 32). */
+  int32_t check_finite;      /* 0 (default).  1 (a debug aid): after the embeddings,
+                                after every block and on the outputs, the sequence rows
+                                of every sample are scanned for NaN and infinity; the
+                                forward then waits for its stream and returns
+                                ZIMG_ENONFINITE naming the first stage whose values were
+                                not finite.  Costs one read of the sequence per block
+                                and makes the forward synchronous. */
 } zimg_dit_config;
 
 /* One named weight tensor handed to the engine.  ``data`` is a HOST

@@ -184,7 +184,11 @@ int zimg_dit_profile_read(zimg_dit* h, zimg_kernel_stat* stats, int32_t max_stat
  *         segments are written
  *   seg   HOST int32 [B][4]: (start, rows) of the first range, (start, rows)
  *         of the second (rows may be 0); starts multiples of 8; each range,
- *         its length rounded up to 64, must lie inside [0, S_pad)
+ *         its length rounded up to 64, must lie inside [0, S_pad).  Keys
+ *         past a range's end enter its last tile with weight 0: the vT
+ *         columns from the end up to the next multiple of 8 must be finite
+ *         (0 * v); further columns, and the k rows of those keys, may hold
+ *         anything (another sample's rows: samples never interact)
  *   workspace  DEVICE, 256-byte aligned, ws_bytes long: the work list and
  *         the partial results of pairs split along keys (caller-owned; no
  *         state survives a call).  zimg_attention_workspace_size() gives

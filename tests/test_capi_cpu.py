@@ -71,6 +71,8 @@ def test_full_manifest_counts():
     ("norm_eps", 0.0, "EINVAL"),
     ("batch_invariant", 2, "EINVAL"),
     ("linear_int8", -1, "EINVAL"),
+    ("token_pad", 16, "EUNSUPPORTED"),
+    ("check_finite", 2, "EINVAL"),
 ])
 def test_config_validation(field, value, code):
     b = _b()
