@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
     return t < nt0 ? min(KTILE, sg.n[0] - t * KTILE) : min(KTILE, sg.n[1] - (t - nt0) * KTILE);
   };
 
-  // Direct global -> LDS loads: a wave's load i fills 1 KB = 64 chunks of 16 B.
+  // Direct loads into LDS: a wave's load i fills 1 KB = 64 chunks of 16 B.
   // K: chunk p -> LDS row R = p/16 (holds key 32*(R/32) + swap_bits23(R%32)),
   //    stored position p%16 holds logical chunk (p%16) ^ (R & 15).
   // V^T: chunk p -> row d = p/8, stored position p%8 holds keys 8*((p%8) ^ ((d>>1)&7)).

@@ -72,7 +72,7 @@ ZI_DEV uint32_t quant4(float a, float b, float c, float d, float inv) {
   return quant_code(a, inv) | (quant_code(b, inv) << 8) | (quant_code(c, inv) << 16) | (quant_code(d, inv) << 24);
 }
 
-// Barrier that publishes direct global->LDS loads: each wave first waits for
+// Barrier that publishes direct loads into LDS: each wave first waits for
 // its own outstanding loads (vmcnt), then all waves meet.  Written out
 // explicitly because the compiler does not always place that wait before a
 // loop-header barrier, and a wave's wait covers only its own loads.

@@ -406,9 +406,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const bf16_t* __restrict__ 
   // A wave's load i fills 1 KB of LDS = 64 chunks of 16 B, chunk p = (i*NW + wid)*64 + lane,
   // i.e. row p/8, stored position p%8; it fetches the logical chunk stored there
   // (rows past M or N are clamped: their results are never stored).
-  // Sources are a per-tile base (uniform: scalar registers) plus a per-lane
-  // 32-bit byte offset that stays fixed for the whole K loop, so the loads
-  // take the scalar-base form and a K-step only advances the two bases.
+  // Sources are the tile's rows of A and W, read through buffer resources,
+  // at a per-lane 32-bit byte offset that stays fixed for the whole K loop;
+  // a K-step only changes the uniform (scalar) offset.
   const char* a_base = reinterpret_cast<const char*>(A + (int64_t)m0 * lda);
   const char* b_base = reinterpret_cast<const char*>(W + (int64_t)n0 * ldw);
   uint32_t a_off[NA];
