@@ -1173,7 +1173,7 @@ int zimg_dit::forward(const float* const* latents, const Layout& L, const void* 
   }
   rc = prof_stop(s);
   if (rc || !c.check_finite) return rc;
-  // check_finite: scan the outputs, then wait for the verdict
+  // check_finite: scan the outputs, then wait for the result
   const int nb_all = (int)blocks.size();
   for (int b = 0; b < L.B; ++b)
     HIP_TRY(zimg::launch_scan_finite(outs[b], (int64_t)c.in_channels * L.Hp[b] * c.patch * L.Wp[b] * c.patch, nb_all + 1,
