@@ -304,11 +304,12 @@ def golden():
             "meta": json.loads(str(z["meta"]))}
 
 
-def _full_forward(linear_int8):
+def _full_forward(linear_int8, workload="dit_1024"):
     torch = _torch()
     from diffusion_transformer_image_amd import binding
-    wl = synthetic.WORKLOADS["dit_1024"]
-    ecfg = helpers.engine_config(wl["model"], max_batch=1, max_image_tokens=4096, max_caption_tokens=512,
+    wl = synthetic.WORKLOADS[workload]
+    n_img = (wl["latent"][2] // 2) * (wl["latent"][3] // 2)
+    ecfg = helpers.engine_config(wl["model"], max_batch=1, max_image_tokens=n_img, max_caption_tokens=512,
                                  linear_int8=linear_int8)
     dit = binding.DiT(ecfg, helpers.engine_weights(ecfg, seed=wl["seed"]).items_parallel(as_bits=True))
     lat_d = torch.from_numpy(synthetic.latent(wl["latent"], seed=wl["seed"])).cuda()
@@ -338,3 +339,22 @@ def test_full_forward_1024_bf16_vs_oracle(golden):
     got = _full_forward(0)
     r, c = helpers.assert_parity(got, golden["float"], "1024 bf16 forward vs the oracle")
     print(f"bf16 engine: rel-L2 {r:.2e} cos {c:.7f} vs float oracle")
+
+
+def test_full_forward_2048_int8_vs_oracle():
+    """The int8 engine's 2048x2048 output (16,384 + 512 tokens, 34 blocks)
+    against the stored float64 oracle output of the same forward: cosine >=
+    0.9996, the pages' int8 figure, as at 1024x1024."""
+    path = os.path.join(os.path.dirname(GOLDEN), "dit_2048_oracle_outputs.npz")
+    if not os.path.exists(path):
+        pytest.skip("stored oracle outputs missing (tests/golden/make_fullsize_outputs.py writes them)")
+    z = np.load(path, allow_pickle=False)
+    meta = json.loads(str(z["meta"]))
+    wl = synthetic.WORKLOADS["dit_2048"]
+    assert meta["latent"] == list(wl["latent"]) and meta["caption_lens"] == list(wl["caption_lens"])
+    got = _full_forward(1, "dit_2048")
+    cf = helpers.cosine(got, z["float"].astype(np.float64))
+    print(f"2048x2048 int8 engine: cosine {cf:.7f}, rel-L2 {helpers.rel_l2(got, z['float'].astype(np.float64)):.2e} "
+          f"vs the float oracle")
+    assert np.isfinite(got).all()
+    assert cf >= INT8_COS_GATE, f"cosine {cf:.7f} against the float oracle"
