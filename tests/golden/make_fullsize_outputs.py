@@ -7,7 +7,9 @@ recompute in its run time, as float16 arrays next to this file:
       2**16: the step-0 model output of the batch (``out0``), the largest
       |w2 output| of every block of that step for each sample (``ffn_peak``,
       float64), and -- with ``--loop`` -- the model output of every step and
-      the final latent after 8 steps (``outs``, ``final``);
+      the final latent after 8 steps (``outs``, ``final``); ``euler_int8``
+      adds the oracle's int8 variant of the step-0 model output
+      (``out0_int8``) to that file;
   dit_2048_oracle_outputs.npz
       the 2048x2048 forward (16,384 image + 512 caption tokens, t = 0.5).
 
@@ -16,6 +18,7 @@ oracle takes about 20 minutes per full-width 1536x640 forward of the pair and
 about an hour for the 2048x2048 forward on an 8-core host:
 
     python tests/golden/make_fullsize_outputs.py euler [--loop]
+    python tests/golden/make_fullsize_outputs.py euler_int8
     python tests/golden/make_fullsize_outputs.py dit_2048
 """
 
@@ -81,6 +84,33 @@ def euler(loop):
     print(json.dumps(meta, indent=1))
 
 
+def euler_int8():
+    """The int8 variant's step-0 model output of the Euler workload, added
+    to the stored file of the float runs (which it leaves as they are)."""
+    name = "euler_1536x640"
+    path = os.path.join(HERE, f"{name}_oracle_outputs.npz")
+    z = np.load(path, allow_pickle=False)
+    arrays = {k: z[k] for k in z.files if k != "meta"}
+    meta = json.loads(str(z["meta"]))
+    wl = synthetic.WORKLOADS[name]
+    cfg = ModelConfig.from_dict(wl["model"])
+    W = synthetic.SyntheticWeights(manifest(cfg), seed=wl["seed"], outlier_log2=wl["outlier_log2"])
+    lat = synthetic.latent(wl["latent"], seed=wl["seed"])
+    caps = synthetic.captions(wl["caption_lens"], seed=wl["seed"])
+    sig, t = osm.schedule(wl["steps"], wl["shift"])
+    t0 = np.full(lat.shape[0], np.float32(t[0]), dtype=np.float64)
+    start = time.time()
+    out = om.forward(cfg, W, lat, caps, t0, quant="int8")
+    secs = time.time() - start
+    ref = arrays["out0"].astype(np.float64)
+    cos = float(np.sum(out * ref) / np.sqrt(np.sum(out * out) * np.sum(ref * ref)))
+    print(f"int8 step 0: {secs:.1f} s, cosine {cos:.7f} against the stored float output", flush=True)
+    arrays["out0_int8"] = out.astype(np.float16)
+    meta["int8_step0_vs_float_cosine"] = cos
+    meta.setdefault("seconds", {})["step0_int8"] = secs
+    np.savez(path, meta=np.array(json.dumps(meta)), **arrays)
+
+
 def dit_2048():
     name = "dit_2048"
     wl = synthetic.WORKLOADS[name]
@@ -102,6 +132,8 @@ if __name__ == "__main__":
     what = sys.argv[1] if len(sys.argv) > 1 else ""
     if what == "euler":
         euler("--loop" in sys.argv[2:])
+    elif what == "euler_int8":
+        euler_int8()
     elif what == "dit_2048":
         dit_2048()
     else:

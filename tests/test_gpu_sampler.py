@@ -131,6 +131,45 @@ def test_euler_loop_full_size_vs_stored_oracle():
     dit.close()
 
 
+def test_euler_step0_full_size_int8_vs_stored_oracle():
+    """Int8 block projections on the full-width Euler workload (1536x640,
+    batch 2, captions 77 / 300, w2 outliers): the step-0 model output of the
+    batch is as close to the float64 output as the oracle's own int8 variant
+    of that step (stored next to the float runs) is, up to a fifth of the
+    scheme's own loss.
+
+    Here the int8 scheme itself loses accuracy: after the first block the
+    residual carries the w2 outlier channels (about 30x the row rms), so the
+    per-token scale of every later block input is set by them and the rest
+    of each row keeps only a few quantization levels (input error 4 % after
+    two blocks against 1 % without outliers).  With steps that coarse, the
+    engine and the oracle (whose fp32 / bf16 values feeding each quantizer
+    differ at the 1e-3 level) take many code decisions differently, so the
+    two int8 results are compared through their distance to the float output
+    rather than element by element at the int8 bar of ordinary rows."""
+    torch = _torch()
+    wl = synthetic.WORKLOADS["euler_1536x640"]
+    gold, meta = _golden()
+    if gold is None or "out0_int8" not in gold:
+        pytest.skip("the oracle's int8 step-0 output is not stored (make_fullsize_outputs.py euler_int8)")
+    lens, shape = wl["caption_lens"], wl["latent"]
+    dit = _engine(wl["model"], 2, (shape[2] // 2) * (shape[3] // 2), max(lens), wl["outlier_log2"], linear_int8=1)
+    x = torch.from_numpy(synthetic.latent(shape, seed=wl["seed"])).cuda()
+    caps = torch.from_numpy(np.concatenate(synthetic.captions(lens, seed=wl["seed"]))).cuda()
+    t0 = float(np.float32(meta["t0"]))
+    out = torch.empty_like(x)
+    dit.forward(x, caps, lens, (t0, t0), out)
+    torch.cuda.synchronize()
+    dit.close()
+    got = out.cpu().numpy()
+    assert np.isfinite(got).all()
+    ref_f, ref_q = gold["out0"].astype(np.float64), gold["out0_int8"].astype(np.float64)
+    cf, co = helpers.cosine(got, ref_f), meta["int8_step0_vs_float_cosine"]
+    print(f"int8 step 0: cosine vs the float oracle: engine {cf:.7f}, oracle's int8 variant {co:.7f}; engine vs the "
+          f"int8 oracle: rel-L2 {helpers.rel_l2(got, ref_q):.2e} cos {helpers.cosine(got, ref_q):.6f}")
+    assert cf >= co - (1.0 - co) / 5, f"engine int8 cosine {cf:.7f} vs the oracle's int8 variant {co:.7f}"
+
+
 def test_euler_loop_full_size_reproducible_and_batch_independent():
     torch = _torch()
     from diffusion_transformer_image_amd import euler_loop
