@@ -27,54 +27,66 @@ __global__ void timestep_embed_kernel(TimeArgs ta, int B, int dim, float t_scale
   out[idx] = (float)(i < half ? cos(arg) : sin(arg));
 }
 
-// y[b][n] = sum_k W[n][k] act(x[b][k]) + bias[n].  32 lanes per output row,
-// 16-byte weight loads; up to 8 samples per launch share each weight read.
+// y[b][n] = sum_k W[n][k] act(x[b][k]) + bias[n].  A group of 32 lanes owns
+// GEMV_R consecutive output rows and reads them with one 16-byte weight load
+// per lane and row, all in flight together; act(x) of a K-chunk is computed
+// once for the group's rows.  NB samples (up to 8 per launch) share each
+// weight read.
 constexpr int GEMV_MAXB = 8;
+constexpr int GEMV_R = 4;
 
+template <int NB>
 __global__ __launch_bounds__(256) void gemv_kernel(const bf16_t* __restrict__ W, const float* __restrict__ bias,
                                                    const float* __restrict__ x, int64_t ldx, float* __restrict__ y,
-                                                   int64_t ldy, int N, int K, int B, int act) {
-  const int lane = threadIdx.x & 63;
-  const int n = (blockIdx.x * 256 + threadIdx.x) >> 5;  // 8 rows per workgroup
-  const int sub = lane & 31;
-  float acc[GEMV_MAXB];
+                                                   int64_t ldy, int N, int K, int act) {
+  const int sub = threadIdx.x & 31;
+  const int n0 = ((blockIdx.x * 256 + threadIdx.x) >> 5) * GEMV_R;
+  float acc[GEMV_R][NB];
 #pragma unroll
-  for (int b = 0; b < GEMV_MAXB; ++b) acc[b] = 0.f;
-  if (n < N) {
-    const bf16_t* wr = W + (int64_t)n * K;
-    for (int k = sub * 8; k < K; k += 256) {
-      const u32x4 u = *reinterpret_cast<const u32x4*>(wr + k);
-      float w[8];
+  for (int r = 0; r < GEMV_R; ++r)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        w[2 * q] = __uint_as_float(u[q] << 16);
-        w[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
-      }
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+  for (int k = sub * 8; k < K; k += 256) {
+    u32x4 u[GEMV_R];
 #pragma unroll
-      for (int b = 0; b < GEMV_MAXB; ++b) {
-        if (b >= B) break;
-        const float* xb = x + b * ldx + k;
-        const float4 x0 = *reinterpret_cast<const float4*>(xb);
-        const float4 x1 = *reinterpret_cast<const float4*>(xb + 4);
-        float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int r = 0; r < GEMV_R; ++r)
+      u[r] = n0 + r < N ? *reinterpret_cast<const u32x4*>(W + (int64_t)(n0 + r) * K + k) : u32x4{0, 0, 0, 0};
+    float xv[NB][8];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float4 x0 = *reinterpret_cast<const float4*>(x + b * ldx + k);
+      const float4 x1 = *reinterpret_cast<const float4*>(x + b * ldx + k + 4);
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xv[b][q] = act ? v[q] / (1.0f + __expf(-v[q])) : v[q];
+    }
+#pragma unroll
+    for (int r = 0; r < GEMV_R; ++r)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
         float s = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float v = act ? xv[q] / (1.0f + __expf(-xv[q])) : xv[q];
-          s = fmaf(w[q], v, s);
+        for (int q = 0; q < 4; ++q) {
+          s = fmaf(__uint_as_float(u[r][q] << 16), xv[b][2 * q], s);
+          s = fmaf(__uint_as_float(u[r][q] & 0xffff0000u), xv[b][2 * q + 1], s);
         }
-        acc[b] += s;
+        acc[r][b] += s;
       }
-    }
   }
 #pragma unroll
-  for (int b = 0; b < GEMV_MAXB; ++b) {
+  for (int r = 0; r < GEMV_R; ++r)
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) acc[b] += __shfl_xor(acc[b], o, 64);
-  }
-  if (n < N && sub == 0) {
-    const float bv = bias ? bias[n] : 0.f;
-    for (int b = 0; b < B; ++b) y[b * ldy + n] = acc[b] + bv;
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int o = 16; o > 0; o >>= 1) acc[r][b] += __shfl_xor(acc[r][b], o, 64);
+  if (sub == 0) {
+#pragma unroll
+    for (int r = 0; r < GEMV_R; ++r)
+      if (n0 + r < N) {
+        const float bv = bias ? bias[n0 + r] : 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) y[b * ldy + n0 + r] = acc[r][b] + bv;
+      }
   }
 }
 
@@ -136,10 +148,23 @@ hipError_t launch_timestep_embed(const TimeArgs& t, int B, int dim, float t_scal
 
 hipError_t launch_gemv(const bf16_t* W, const float* bias, const float* x, int64_t ldx, float* y, int64_t ldy,
                        int N, int K, int B, int act, hipStream_t s) {
+  const dim3 grid((unsigned)((N + 8 * GEMV_R - 1) / (8 * GEMV_R))), blk(256);
   for (int b0 = 0; b0 < B; b0 += GEMV_MAXB) {
     const int nb = B - b0 < GEMV_MAXB ? B - b0 : GEMV_MAXB;
-    hipLaunchKernelGGL(gemv_kernel, dim3((N + 7) / 8), dim3(256), 0, s, W, bias, x + b0 * ldx, ldx, y + b0 * ldy,
-                       ldy, N, K, nb, act);
+    const float* xb = x + b0 * ldx;
+    float* yb = y + b0 * ldy;
+#define GV(NB_) hipLaunchKernelGGL(gemv_kernel<NB_>, grid, blk, 0, s, W, bias, xb, ldx, yb, ldy, N, K, act)
+    switch (nb) {
+      case 1: GV(1); break;
+      case 2: GV(2); break;
+      case 3: GV(3); break;
+      case 4: GV(4); break;
+      case 5: GV(5); break;
+      case 6: GV(6); break;
+      case 7: GV(7); break;
+      default: GV(8); break;
+    }
+#undef GV
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
