@@ -122,6 +122,16 @@ def test_forward_small_varlen_batch():
     print(rep)
 
 
+def test_forward_batch_past_one_conditioning_launch():
+    """B = 10, each sample with its own timestep and caption length: the adaLN
+    GEMV takes up to 8 samples per launch, so samples 8 and 9 go through a
+    second launch; every sample's blocks and output against the oracle."""
+    lens = (3, 17, 1, 40, 8, 25, 64, 2, 33, 11)
+    t = tuple(0.05 + 0.09 * i for i in range(10))
+    rep, _ = _compare_forward(SMALL, (10, 16, 4, 6), lens, t, 6, 64)
+    print(rep[-3:])
+
+
 @pytest.mark.parametrize("latent,lens", [
     ((1, 16, 2, 2), (1,)),                # one image token, one caption token
     ((3, 16, 4, 6), (1, 77, 33)),         # 6 image tokens; captions of 1, 77 and 33 tokens
