@@ -135,9 +135,12 @@ def summarize(stats, steps, work, int8=False):
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(wl, model):
-    """Time the float64 oracle on one joint block of the workload (all rows),
-    then scale to a whole forward by the algorithmic FLOP ratio (an
-    extrapolation, labelled as such, with the host CPU model and BLAS)."""
+    """Time the float64 oracle on a bounded sample of the workload: one block
+    of each kind on its own rows (a noise-refiner block on the image tokens, a
+    context-refiner block on the caption tokens, a joint block on all of
+    them) plus the embedders and the final layer, and sum the blocks by their
+    counts in the stack (an estimate of one forward, labelled as such, with
+    the host CPU model and BLAS)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -150,15 +153,19 @@ def cpu_baseline(wl, model):
     Hp, Wp = lat_shape[2] // 2, lat_shape[3] // 2
     n_img, L = Hp * Wp, lens[0]
     S = n_img + L
+    prefixes = {"noise_refiner": "noise_refiner.0", "context_refiner": "context_refiner.0", "layers": "layers.0"}
     W = synthetic.SyntheticWeights(manifest(cfg), seed=wl["seed"])
-    p = "layers.0"
-    need = [n for n, _ in manifest(cfg) if n.startswith(p + ".") or n.startswith("t_embedder.")]
-    Wb = {n: W[n] for n in need}
+    keep = tuple(p + "." for p in prefixes.values()) + ("t_embedder.", "all_x_embedder.", "cap_embedder.",
+                                                        "all_final_layer.")
+    Wb = {n: W[n] for n, _ in manifest(cfg) if n.startswith(keep)}
+    lat = synthetic.latent(lat_shape, seed=wl["seed"])[0].astype(np.float64)
+    feats = synthetic.captions(lens, seed=wl["seed"])[0].astype(np.float64)
     x = synthetic.residual((S, cfg.hidden), seed=wl["seed"]).astype(np.float64)
     cap_ids, img_ids = om.position_ids(L, Hp, Wp)
-    cos, sin = om.rope_tables(cfg, np.concatenate([img_ids, cap_ids]))
+    cos_img, sin_img = om.rope_tables(cfg, img_ids)
+    cos_cap, sin_cap = om.rope_tables(cfg, cap_ids)
+    cos, sin = np.concatenate([cos_img, cos_cap]), np.concatenate([sin_img, sin_cap])
     c = om.timestep_mlp(cfg, Wb, np.array([wl["t"][0]]))[0]
-    mod = om.block_modulation(Wb, p, c)
     blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
     threads = max([d.get("num_threads", 1) for d in blas] or [1])
     blas_name = ", ".join(sorted({f"{d.get('internal_api', '?')} {d.get('version', '')}".strip() for d in blas})) or "unknown"
@@ -171,19 +178,31 @@ def cpu_baseline(wl, model):
                     break
     except OSError:
         pass
-    t0 = time.perf_counter()
-    om.block(cfg, Wb, p, x, cos, sin, mod)
-    block_s = time.perf_counter() - t0
-    w = work_per_forward(model, n_img, lens)
-    fwd_flops = sum(w[k] for k in MFMA_CLASSES)
-    Dm, Fm = model["hidden"], model["ffn"]
-    joint_flops = 2.0 * S * Dm * (4 * Dm + 3 * Fm) + 4.0 * S * S * Dm
-    fwd_s = block_s * fwd_flops / joint_flops
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    n_noise, n_ctx, n_joint = cfg.n_noise_refiner, cfg.n_context_refiner, cfg.n_layers
+    p = prefixes["noise_refiner"]  # a kind absent from the stack is not timed
+    t_noise = timed(lambda: om.block(cfg, Wb, p, x[:n_img], cos_img, sin_img,
+                                     om.block_modulation(Wb, p, c))) if n_noise else 0.0
+    p = prefixes["context_refiner"]
+    t_ctx = timed(lambda: om.block(cfg, Wb, p, x[n_img:], cos_cap, sin_cap, None)) if n_ctx else 0.0
+    p = prefixes["layers"]
+    t_joint = timed(lambda: om.block(cfg, Wb, p, x, cos, sin, om.block_modulation(Wb, p, c))) if n_joint else 0.0
+    t_ends = timed(lambda: (om.x_embed(cfg, Wb, lat), om.cap_embed(cfg, Wb, feats),
+                            om.final_layer(cfg, Wb, x[:n_img], c)))
+    fwd_s = n_noise * t_noise + n_ctx * t_ctx + n_joint * t_joint + t_ends
+    sample_s = t_noise + t_ctx + t_joint + t_ends
     return {"value": round(S / fwd_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu": cpu_model, "blas": blas_name, "precision": "float64",
-            "sample": (f"extrapolation: one float64 joint block of the forward (all {S} rows, hidden {Dm}) "
-                       f"timed at {block_s:.2f} s, scaled to the whole forward by the algorithmic FLOP ratio "
-                       f"({fwd_flops / joint_flops:.2f} x the block); the whole forward never ran on the CPU")}
+            "sample": (f"estimate from a {sample_s:.1f} s float64 sample: one block of each kind on its own rows "
+                       f"(noise refiner, {n_img} image rows: {t_noise:.2f} s; context refiner, {L} caption rows: "
+                       f"{t_ctx:.2f} s; joint, all {S} rows: {t_joint:.2f} s) and the embedders + final layer "
+                       f"({t_ends:.2f} s); forward = {n_noise} x noise + {n_ctx} x context + {n_joint} x joint + "
+                       f"embedders and final layer = {fwd_s:.1f} s; the whole forward never ran on the CPU")}
 
 
 # ---------------------------------------------------------------- traffic from committed counters
