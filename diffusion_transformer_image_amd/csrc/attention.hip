@@ -278,8 +278,9 @@ __global__ __launch_bounds__(256, 2) void attention_kernel(AttnArgs a) {
   // The first NPRE score MFMAs of the next tile are issued before the row
   // maxima of the current one, so that dependent chain (16 three-way maxima,
   // the lane-pair exchange, the ceiling) runs while they execute: -1.7 % per
-  // launch against starting the scores after it.
-  constexpr int NPRE = 4;
+  // launch against starting the scores after it with NPRE = 4, a further
+  // 0.4-0.9 % with 8 (10 and 12 are slower).
+  constexpr int NPRE = 8;
   constexpr int EXPV = (64 + (16 - NPRE) - 1) / (16 - NPRE);  // exponential-phase VALU per score MFMA
   auto pin_pre = [&]() {
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // first K operand reads
